@@ -1,0 +1,284 @@
+"""Benchmark of one GVA decode step on one MI355X.
+
+A step is the whole hot path over one batch: append each sequence's new token
+(values + rotated positional key), absorb the per-head maps into the queries,
+and run split-context decode attention with its merge.  The default workload
+is the 350M-shaped decode: B=32, H=16, G=4, d_h=64, d_n=48, d_r=16, T=4096,
+bf16 caches.  Inputs are synthetic and resident in HBM before timing starts;
+the caches are cycled over enough copies (>= 1 GiB in total) that no step
+finds its cache in the 256 MB last-level cache.
+
+Prints ONE JSON line.  `value` is cache bytes read per second over whole
+steps; `roofline` covers the decode kernel alone (HIP events around each of
+its launches); `cpu_baseline` is the float64 oracle timed on host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       python bench.py --copy-calibration     (plain copy for counter scaling)
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("decode-attn cache GB/s (% of HBM peak) and queries*ctx/s, "
+          "350M shape, T=4096")
+PEAK_HBM_GBS = 8000.0
+ROTATE_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["compressed_kv_cache_amd/csrc/gva_decode_mfma.hip",
+                  "compressed_kv_cache_amd/csrc/gva_decode_ref.hip",
+                  "compressed_kv_cache_amd/csrc/gva_device.h"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_350m")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gqa", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time for the oracle sample")
+    return ap.parse_args()
+
+
+def copy_calibration(torch, steps):
+    """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
+    n = 256 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n,
+                      "launches": steps}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; "
+                          "--gpus must be 1 (see DESIGN.md for how the path "
+                          "would shard)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        copy_calibration(torch, max(1, args.steps))
+        return
+    import compressed_kv_cache_amd as gva
+    import synthetic as syn
+
+    dev = torch.device("cuda:0")
+    cfg0 = syn.get_config(args.workload)
+    cfg = syn.with_overrides(cfg0, append=True)
+    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    x = syn.make_gva_inputs(cfg, device=dev)
+    lens = x["seq_lens_host"]
+    tokens = int(lens.sum())
+    esize = 2 if cfg.cache_dtype == "bfloat16" else 4
+    bytes_per_token = (cfg.G * cfg.d_h + cfg.d_r) * esize
+    cache_bytes = tokens * bytes_per_token
+    pool_bytes = (x["v_pool"].numel() + x["k_pool"].numel()) * esize
+    R = max(1, math.ceil(ROTATE_BYTES / pool_bytes))
+    pools = [(x["v_pool"], x["k_pool"])]
+    for _ in range(R - 1):
+        pools.append((x["v_pool"].clone(), x["k_pool"].clone()))
+    ws = torch.empty(gva.decode_workspace_bytes(cfg.B, cfg.H, x["v_pool"], x["k_pool"],
+                                                x["block_table"], x["max_seq_len"]),
+                     dtype=torch.uint8, device=dev)
+    qa = torch.empty((cfg.B, cfg.H, cfg.d_h + cfg.d_r), dtype=torch.float32, device=dev)
+    out = torch.empty((cfg.B, cfg.H, cfg.d_h), dtype=torch.float32, device=dev)
+    lse = torch.empty((cfg.B, cfg.H), dtype=torch.float32, device=dev)
+
+    def step(i, ev=None):
+        vp, kp = pools[i % R]
+        gva.append_cache(x["v_new"], x["k_new"], x["pos"], x["block_table"], vp, kp,
+                         rope_base=cfg.rope_base)
+        gva.absorb_query(x["q_nope"], x["q_rope"], x["M"], x["pos"],
+                         rope_base=cfg.rope_base, out=qa)
+        if ev is not None:
+            ev[0].record()
+        gva.decode_attention(qa, vp, kp, x["block_table"], x["seq_lens"],
+                             x["max_seq_len"], workspace=ws, out=out, lse=lse)
+        if ev is not None:
+            ev[1].record()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # whole steps, one event pair around K steps
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # decode launches alone, an event pair around each launch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    dec_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+    dec_med_ms = dec_ms[len(dec_ms) // 2]
+    print(f"[bench] step {ms_per_step * 1e3:.2f} us, decode avg {dec_avg_ms * 1e3:.2f} us",
+          file=sys.stderr, flush=True)
+
+    value = cache_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = cache_bytes / (dec_avg_ms * 1e-3) / 1e9
+
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        rec = tr.get(cfg.name)
+        if rec and rec.get("kernel_source_hash") == kernel_source_hash():
+            traffic = rec.get("bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+
+    extra = {
+        "queries_ctx_per_s": tokens / (ms_per_step * 1e-3),
+        "head_queries_ctx_per_s": cfg.H * tokens / (ms_per_step * 1e-3),
+        "pct_of_hbm_peak": 100.0 * value / PEAK_HBM_GBS,
+        "decode_us_avg": dec_avg_ms * 1e3,
+        "decode_us_median": dec_med_ms * 1e3,
+        "decode_GBps": achieved,
+        "cache_bytes_per_step": cache_bytes,
+        "gqa_cache_bytes_same_shape": tokens * 2 * cfg.G * cfg.d_h * esize,
+    }
+
+    if not args.no_gqa and cfg.cache_dtype == "bfloat16":
+        extra["gqa"] = bench_gqa(torch, gva, syn, cfg0, dev, args.steps, args.warmup)
+        extra["gqa"]["time_ratio_gva_over_gqa"] = dec_avg_ms * 1e3 / extra["gqa"]["us_avg"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg0, x, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.cache_dtype == "bfloat16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name, "B": cfg.B, "H": cfg.H, "G": cfg.G, "d_h": cfg.d_h,
+            "d_n": cfg.d_n, "d_r": cfg.d_r,
+            "T": cfg.T if cfg.T else "ragged",
+            "context_tokens": tokens, "cache_dtype": cfg.cache_dtype,
+            "accumulate": "f32",
+            "step": "append+absorb+decode(split+merge)",
+            "rotating_cache_copies": R,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "kernel": "gva_decode_attention",
+            "algorithmic_bytes_per_launch": cache_bytes,
+        },
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+def bench_gqa(torch, gva, syn, cfg, dev, steps, warmup):
+    """Same-shape GQA decode (key and value streams), same rotation protocol."""
+    y = syn.make_gqa_inputs(cfg, device=dev)
+    esize = 2
+    tokens = int(y["seq_lens_host"].sum())
+    byts = tokens * 2 * cfg.G * cfg.d_h * esize
+    pool_bytes = 2 * y["v_pool"].numel() * esize
+    R = max(1, math.ceil(ROTATE_BYTES / pool_bytes))
+    pools = [(y["k_pool"], y["v_pool"])] + [
+        (y["k_pool"].clone(), y["v_pool"].clone()) for _ in range(R - 1)]
+    out = torch.empty((cfg.B, cfg.H, cfg.d_h), dtype=torch.float32, device=dev)
+    lse = torch.empty((cfg.B, cfg.H), dtype=torch.float32, device=dev)
+    for i in range(warmup):
+        kp, vp = pools[i % R]
+        gva.gqa_decode_attention(y["q"], kp, vp, y["block_table"], y["seq_lens"],
+                                 y["max_seq_len"], out=out, lse=lse)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        kp, vp = pools[i % R]
+        evs[i][0].record()
+        gva.gqa_decode_attention(y["q"], kp, vp, y["block_table"], y["seq_lens"],
+                                 y["max_seq_len"], out=out, lse=lse)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    avg = sum(ms) / len(ms)
+    del pools, y
+    torch.cuda.empty_cache()
+    return {"us_avg": avg * 1e3, "cache_bytes": byts, "GBps": byts / (avg * 1e-3) / 1e9}
+
+
+def cpu_baseline(cfg, x, target_s):
+    """The float64 oracle on the host: whole sequences of the same workload,
+    as many as fit the time target, scaled to cache GB/s."""
+    import numpy as np
+    import oracle as o
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    h = {k: v.detach().cpu() for k, v in x.items() if hasattr(v, "detach")}
+    esize = 2 if cfg.cache_dtype == "bfloat16" else 4
+    per_tok = (cfg.G * cfg.d_h + cfg.d_r) * esize
+    vp, kp = o.to_f64(h["v_pool"]), o.to_f64(h["k_pool"])
+    done_tokens, spent, seqs = 0, 0.0, 0
+    order = list(range(cfg.B))
+    while spent < target_s:
+        b = order[seqs % cfg.B]
+        t = time.perf_counter()
+        o.gva_decode_materialized(h["q_nope"], h["q_rope"], h["M"], vp, kp,
+                                  h["block_table"], h["seq_lens"], base=cfg.rope_base,
+                                  seqs=[b])
+        spent += time.perf_counter() - t
+        done_tokens += int(h["seq_lens_host"][b])
+        seqs += 1
+    gbs = done_tokens * per_tok / spent / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{seqs} whole sequences ({done_tokens} context tokens x {cfg.H} heads)"
+                      f" of {cfg.name}, float64, keys materialised, {spent:.1f} s",
+            "queries_ctx_per_s": done_tokens / spent}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,16 @@
+"""libgva: Grouped Value Attention absorbed decode on MI355X (gfx950).
+
+Importing the package loads the in-tree ``libgva.so`` and fails loudly when it
+is missing; every operation runs in its HIP kernels.
+"""
+from . import _lib
+from ._lib import GvaError, GvaShape, LIB_PATH
+from .ops import (BLOCK_SIZE, absorb_query, append_cache, cache_scalars_per_token,
+                  decode_attention, decode_workspace_bytes, gqa_decode_attention,
+                  make_shape)
+
+lib = _lib.load()
+
+__all__ = ["BLOCK_SIZE", "GvaError", "GvaShape", "LIB_PATH", "absorb_query",
+           "append_cache", "cache_scalars_per_token", "decode_attention",
+           "decode_workspace_bytes", "gqa_decode_attention", "lib", "make_shape"]

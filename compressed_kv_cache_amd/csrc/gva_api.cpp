@@ -1,0 +1,239 @@
+// libgva C ABI: host-side validation and dispatch.  Every check here runs
+// before any HIP call, so argument errors are reported synchronously and
+// can be exercised without a GPU.
+#include <math.h>
+#include <stdint.h>
+
+#include "gva.h"
+#include "gva_internal.h"
+
+namespace gva {
+size_t decode_ref_smem_bytes(int H, int dq);
+hipError_t launch_decode_ref(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
+                             hipStream_t stream);
+bool mfma_decode_supported(const gva_shape& s, bool keys_separate);
+DecodePlan plan_mfma_decode(const gva_shape& s, int max_seq_len, bool keys_separate);
+hipError_t launch_decode_mfma(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
+                              hipStream_t stream);
+}  // namespace gva
+
+namespace {
+
+constexpr int kBlockSize = 64;
+constexpr int kRefThreads = 256;
+constexpr int kRefAccMax = 32;
+constexpr size_t kRefSmemMax = 64 * 1024;
+constexpr int kTargetBlocks = 1024;  // split-chunk target for the reference kernel
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dh_ok(int d_h) { return d_h == 32 || d_h == 64 || d_h == 128; }
+
+// Checks shared by every entry point that reads the paged caches.
+gva_status check_cache_shape(const gva_shape& s) {
+  if (s.B < 0 || s.H < 1 || s.G < 1 || s.d_h < 1) return GVA_ERR_SHAPE;
+  if (s.H % s.G) return GVA_ERR_SHAPE;
+  if (s.block_size != kBlockSize) return GVA_ERR_UNSUPPORTED;
+  if (s.max_blocks < 1 || s.num_blocks < 1) return GVA_ERR_SHAPE;
+  if (s.cache_dtype != GVA_F32 && s.cache_dtype != GVA_BF16) return GVA_ERR_UNSUPPORTED;
+  if (!dh_ok(s.d_h)) return GVA_ERR_UNSUPPORTED;
+  return GVA_OK;
+}
+
+gva_status check_rope_width(int d_r) {
+  if (d_r < 1) return GVA_ERR_SHAPE;
+  if (d_r % 2 || d_r > 64) return GVA_ERR_UNSUPPORTED;
+  return GVA_OK;
+}
+
+gva_status to_status(hipError_t e) { return e == hipSuccess ? GVA_OK : GVA_ERR_HIP; }
+
+int round_up(long long x, int m) { return static_cast<int>(((x + m - 1) / m) * m); }
+
+gva::DecodePlan plan_ref(const gva_shape& s, int max_seq_len) {
+  gva::DecodePlan p{};
+  p.kernel = gva::kKernelRef;
+  const long long total = static_cast<long long>(s.B) * (max_seq_len > 0 ? max_seq_len : 1);
+  int chunk = round_up((total + kTargetBlocks - 1) / kTargetBlocks, kBlockSize);
+  if (chunk < kBlockSize) chunk = kBlockSize;
+  p.chunk_tokens = chunk;
+  p.num_chunks = max_seq_len > 0 ? (max_seq_len + chunk - 1) / chunk : 1;
+  p.partial_floats = static_cast<size_t>(s.B) * p.num_chunks * s.H * (s.d_h + 2);
+  p.workspace_bytes = p.partial_floats * sizeof(float);
+  return p;
+}
+
+gva_status ref_supported(const gva_shape& s, bool keys_separate) {
+  const int dq = keys_separate ? s.d_h : s.d_h + s.d_r;
+  if (static_cast<long long>(s.H) * s.d_h > kRefThreads * kRefAccMax) return GVA_ERR_UNSUPPORTED;
+  if (gva::decode_ref_smem_bytes(s.H, dq) > kRefSmemMax) return GVA_ERR_UNSUPPORTED;
+  return GVA_OK;
+}
+
+// Picks the kernel for a decode call; fails when neither kernel covers it.
+gva_status make_plan(const gva_shape& s, int max_seq_len, bool keys_separate,
+                     gva::DecodePlan* plan) {
+  if (gva::mfma_decode_supported(s, keys_separate)) {
+    *plan = gva::plan_mfma_decode(s, max_seq_len, keys_separate);
+    return GVA_OK;
+  }
+  gva_status st = ref_supported(s, keys_separate);
+  if (st != GVA_OK) return st;
+  *plan = plan_ref(s, max_seq_len);
+  return GVA_OK;
+}
+
+gva_status check_decode_args(const gva_shape* shape, int32_t max_seq_len, bool keys_separate) {
+  if (!shape) return GVA_ERR_NULL;
+  gva_status st = check_cache_shape(*shape);
+  if (st != GVA_OK) return st;
+  if (!keys_separate) {
+    st = check_rope_width(shape->d_r);
+    if (st != GVA_OK) return st;
+  }
+  if (max_seq_len < 0) return GVA_ERR_SHAPE;
+  if (static_cast<long long>(max_seq_len) >
+      static_cast<long long>(shape->max_blocks) * shape->block_size)
+    return GVA_ERR_SHAPE;
+  return GVA_OK;
+}
+
+gva_status workspace_size(const gva_shape* shape, int32_t max_seq_len, bool keys_separate,
+                          size_t* bytes) {
+  if (!bytes) return GVA_ERR_NULL;
+  gva_status st = check_decode_args(shape, max_seq_len, keys_separate);
+  if (st != GVA_OK) return st;
+  gva::DecodePlan plan;
+  st = make_plan(*shape, max_seq_len, keys_separate, &plan);
+  if (st != GVA_OK) return st;
+  *bytes = plan.workspace_bytes;
+  return GVA_OK;
+}
+
+gva_status decode(const gva_shape* shape, const float* q, float q_scale, const void* k_pool,
+                  const void* v_pool, const int32_t* block_table, const int32_t* seq_lens,
+                  int32_t max_seq_len, void* workspace, size_t workspace_bytes, float* out,
+                  float* lse, void* stream, bool keys_separate) {
+  gva_status st = check_decode_args(shape, max_seq_len, keys_separate);
+  if (st != GVA_OK) return st;
+  const gva_shape& s = *shape;
+  gva::DecodePlan plan;
+  st = make_plan(s, max_seq_len, keys_separate, &plan);
+  if (st != GVA_OK) return st;
+  if (s.B == 0) return GVA_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out) return GVA_ERR_NULL;
+  if (plan.workspace_bytes && !workspace) return GVA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
+      (workspace && !aligned16(workspace)))
+    return GVA_ERR_ALIGN;
+  if (workspace_bytes < plan.workspace_bytes) return GVA_ERR_WORKSPACE;
+  gva::DecodeArgs a{};
+  a.q = q;
+  a.v_pool = v_pool;
+  a.k_pool = k_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.max_seq_len = max_seq_len;
+  a.partials = static_cast<float*>(workspace);
+  a.out = out;
+  a.lse = lse;
+  a.q_scale = q_scale;
+  a.keys_separate = keys_separate;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  if (plan.kernel == gva::kKernelMfma) return to_status(gva::launch_decode_mfma(s, plan, a, strm));
+  return to_status(gva::launch_decode_ref(s, plan, a, strm));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gva_abi_version(void) { return GVA_ABI_VERSION; }
+
+const char* gva_status_string(int32_t status) {
+  switch (status) {
+    case GVA_OK: return "ok";
+    case GVA_ERR_NULL: return "a required pointer is NULL";
+    case GVA_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case GVA_ERR_UNSUPPORTED: return "sizes not supported by this build";
+    case GVA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case GVA_ERR_WORKSPACE: return "workspace too small";
+    case GVA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+uint64_t gva_cache_scalars_per_token(const gva_shape* shape) {
+  if (!shape || shape->G < 0 || shape->d_h < 0 || shape->d_r < 0) return 0;
+  return static_cast<uint64_t>(shape->G) * static_cast<uint64_t>(shape->d_h) +
+         static_cast<uint64_t>(shape->d_r);
+}
+
+gva_status gva_absorb_query(const gva_shape* shape, const float* q_nope, const float* q_rope,
+                            const float* M, const int32_t* pos, float softmax_scale,
+                            float rope_base, float* qa, void* stream) {
+  if (!shape) return GVA_ERR_NULL;
+  const gva_shape& s = *shape;
+  if (s.B < 0 || s.H < 1 || s.d_n < 1) return GVA_ERR_SHAPE;
+  if (!dh_ok(s.d_h)) return GVA_ERR_UNSUPPORTED;
+  if (s.d_n > 256) return GVA_ERR_UNSUPPORTED;
+  gva_status st = check_rope_width(s.d_r);
+  if (st != GVA_OK) return st;
+  if (!(rope_base > 0.f) || !isfinite(rope_base)) return GVA_ERR_SHAPE;
+  if (!isfinite(softmax_scale)) return GVA_ERR_SHAPE;
+  if (s.B == 0) return GVA_OK;
+  if (!q_nope || !q_rope || !M || !pos || !qa) return GVA_ERR_NULL;
+  const float scale = softmax_scale > 0.f ? softmax_scale
+                                          : 1.0f / sqrtf(static_cast<float>(s.d_n + s.d_r));
+  return to_status(gva::launch_absorb(s, q_nope, q_rope, M, pos, scale, rope_base, qa,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+gva_status gva_append_cache(const gva_shape* shape, const float* v_new, const float* k_new,
+                            const int32_t* pos, const int32_t* block_table, float rope_base,
+                            void* v_pool, void* k_pool, void* stream) {
+  if (!shape) return GVA_ERR_NULL;
+  const gva_shape& s = *shape;
+  gva_status st = check_cache_shape(s);
+  if (st != GVA_OK) return st;
+  st = check_rope_width(s.d_r);
+  if (st != GVA_OK) return st;
+  if (!(rope_base > 0.f) || !isfinite(rope_base)) return GVA_ERR_SHAPE;
+  if (s.B == 0) return GVA_OK;
+  if (!v_new || !k_new || !pos || !block_table || !v_pool || !k_pool) return GVA_ERR_NULL;
+  return to_status(gva::launch_append(s, v_new, k_new, pos, block_table, rope_base, v_pool,
+                                      k_pool, static_cast<hipStream_t>(stream)));
+}
+
+gva_status gva_decode_workspace_size(const gva_shape* shape, int32_t max_seq_len,
+                                     size_t* bytes) {
+  return workspace_size(shape, max_seq_len, false, bytes);
+}
+
+gva_status gva_decode_attention(const gva_shape* shape, const float* qa, const void* v_pool,
+                                const void* k_pool, const int32_t* block_table,
+                                const int32_t* seq_lens, int32_t max_seq_len, void* workspace,
+                                size_t workspace_bytes, float* out, float* lse, void* stream) {
+  return decode(shape, qa, 1.0f, k_pool, v_pool, block_table, seq_lens, max_seq_len, workspace,
+                workspace_bytes, out, lse, stream, false);
+}
+
+gva_status gqa_decode_workspace_size(const gva_shape* shape, int32_t max_seq_len,
+                                     size_t* bytes) {
+  return workspace_size(shape, max_seq_len, true, bytes);
+}
+
+gva_status gqa_decode_attention(const gva_shape* shape, const float* q, float softmax_scale,
+                                const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                                float* out, float* lse, void* stream) {
+  if (!isfinite(softmax_scale)) return GVA_ERR_SHAPE;
+  float scale = softmax_scale;
+  if (shape && !(scale > 0.f) && shape->d_h > 0)
+    scale = 1.0f / sqrtf(static_cast<float>(shape->d_h));
+  return decode(shape, q, scale, k_pool, v_pool, block_table, seq_lens, max_seq_len, workspace,
+                workspace_bytes, out, lse, stream, true);
+}
+
+}  // extern "C"

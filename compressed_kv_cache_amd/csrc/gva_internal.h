@@ -1,0 +1,55 @@
+// Host-side launchers behind the libgva C ABI.  Arguments have already been
+// validated by gva_api.cpp; each launcher only enqueues kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gva.h"
+
+namespace gva {
+
+// How a decode call splits each sequence's context.
+struct DecodePlan {
+  int kernel;        // kKernel* below
+  int chunk_tokens;  // tokens per split chunk (multiple of the block size)
+  int num_chunks;    // chunks per sequence = ceil(max_seq_len / chunk_tokens)
+  size_t partial_floats;  // floats of split partial results
+  size_t workspace_bytes;
+};
+
+enum { kKernelRef = 0, kKernelMfma = 1 };
+
+DecodePlan plan_gva_decode(const gva_shape& s, int max_seq_len);
+DecodePlan plan_gqa_decode(const gva_shape& s, int max_seq_len);
+
+hipError_t launch_absorb(const gva_shape& s, const float* q_nope, const float* q_rope,
+                         const float* M, const int32_t* pos, float scale, double base,
+                         float* qa, hipStream_t stream);
+
+hipError_t launch_append(const gva_shape& s, const float* v_new, const float* k_new,
+                         const int32_t* pos, const int32_t* block_table, double base,
+                         void* v_pool, void* k_pool, hipStream_t stream);
+
+// GVA decode (keys_separate = false: the key of head h is [V_g(h) | k_rope],
+// query already scaled) and GQA decode (keys_separate = true: key K_g(h),
+// query scaled by `scale` inside the kernel) share one launcher.
+struct DecodeArgs {
+  const float* q;         // qa [B][H][d_h+d_r] or q [B][H][d_h]
+  const void* v_pool;
+  const void* k_pool;     // k_rope pool (GVA) or key pool (GQA)
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int max_seq_len;
+  float* partials;
+  float* out;
+  float* lse;
+  float q_scale;          // multiplies q inside the kernel
+  bool keys_separate;
+};
+
+hipError_t launch_decode(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
+                         hipStream_t stream);
+
+}  // namespace gva

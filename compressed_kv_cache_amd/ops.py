@@ -1,0 +1,195 @@
+"""Python entry points with the C ABI's names.
+
+Argument marshalling only: each function checks that the torch tensors have
+the dtype, device and layout the C ABI documents, builds the size struct and
+calls libgva on torch's current HIP stream.  All arithmetic runs in the HIP
+kernels; there is no other implementation to fall back to.
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import GvaShape, check
+
+BLOCK_SIZE = 64
+
+_CACHE_DTYPES = {torch.float32: _lib.GVA_F32, torch.bfloat16: _lib.GVA_BF16}
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, name, dtype, device, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _cache_dtype(pool, name):
+    if pool.dtype not in _CACHE_DTYPES:
+        raise TypeError(f"{name} must be float32 or bfloat16, got {pool.dtype}")
+    return _CACHE_DTYPES[pool.dtype]
+
+
+def make_shape(B, H, G, d_h, d_n, d_r, max_blocks=1, num_blocks=1,
+               cache_dtype=torch.bfloat16, block_size=BLOCK_SIZE):
+    return GvaShape(B, H, G, d_h, d_n, d_r, block_size, max_blocks, num_blocks,
+                    _CACHE_DTYPES.get(cache_dtype, -1))
+
+
+def cache_scalars_per_token(G, d_h, d_r):
+    """G*d_h + d_r persistent scalars per cached token (computed by libgva)."""
+    s = make_shape(1, G, G, d_h, 1, d_r)
+    return int(_lib.load().gva_cache_scalars_per_token(ctypes.byref(s)))
+
+
+def absorb_query(q_nope, q_rope, M, pos, softmax_scale=None, rope_base=10000.0,
+                 out=None):
+    """qa[B,H,d_h+d_r] = s * [q_nope M_h^T | R(pos) q_rope] (gva_absorb_query)."""
+    dev = q_nope.device
+    _need(q_nope, "q_nope", torch.float32, dev, 3)
+    B, H, d_n = q_nope.shape
+    _need(q_rope, "q_rope", torch.float32, dev, 3)
+    _need(M, "M", torch.float32, dev, 3)
+    _need(pos, "pos", torch.int32, dev, 1)
+    d_r = q_rope.shape[2]
+    d_h = M.shape[1]
+    if tuple(q_rope.shape[:2]) != (B, H) or tuple(M.shape) != (H, d_h, d_n) \
+            or pos.shape[0] != B:
+        raise ValueError("inconsistent shapes for absorb_query")
+    if out is None:
+        out = torch.empty((B, H, d_h + d_r), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev, 3)
+    s = make_shape(B, H, 1, d_h, d_n, d_r)
+    st = _lib.load().gva_absorb_query(
+        ctypes.byref(s), _ptr(q_nope), _ptr(q_rope), _ptr(M), _ptr(pos),
+        float(softmax_scale or 0.0), float(rope_base), _ptr(out), _stream(dev))
+    check("gva_absorb_query", st)
+    return out
+
+
+def append_cache(v_new, k_new, pos, block_table, v_pool, k_pool,
+                 rope_base=10000.0):
+    """Write each sequence's new token (values, rotated k_rope) in place."""
+    dev = v_pool.device
+    _need(v_new, "v_new", torch.float32, dev, 3)
+    _need(k_new, "k_new", torch.float32, dev, 2)
+    _need(pos, "pos", torch.int32, dev, 1)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    cdt = _cache_dtype(v_pool, "v_pool")
+    _need(v_pool, "v_pool", v_pool.dtype, dev, 4)
+    _need(k_pool, "k_pool", v_pool.dtype, dev, 3)
+    NB, bs, G, d_h = v_pool.shape
+    B = v_new.shape[0]
+    d_r = k_pool.shape[2]
+    if tuple(v_new.shape) != (B, G, d_h) or tuple(k_new.shape) != (B, d_r) \
+            or k_pool.shape[0] != NB or k_pool.shape[1] != bs \
+            or block_table.shape[0] != B or pos.shape[0] != B:
+        raise ValueError("inconsistent shapes for append_cache")
+    s = GvaShape(B, G, G, d_h, 1, d_r, bs, block_table.shape[1], NB, cdt)
+    st = _lib.load().gva_append_cache(
+        ctypes.byref(s), _ptr(v_new), _ptr(k_new), _ptr(pos), _ptr(block_table),
+        float(rope_base), _ptr(v_pool), _ptr(k_pool), _stream(dev))
+    check("gva_append_cache", st)
+
+
+def _decode_shape(B, H, v_pool, d_r, block_table, keys_separate=False):
+    NB, bs, G, d_h = v_pool.shape
+    cdt = _cache_dtype(v_pool, "v_pool")
+    return GvaShape(B, H, G, d_h, 1, d_r, bs, block_table.shape[1], NB, cdt)
+
+
+def decode_workspace_bytes(B, H, v_pool, k_pool, block_table, max_seq_len):
+    """Workspace size gva_decode_attention needs for these caches."""
+    s = _decode_shape(B, H, v_pool, k_pool.shape[2], block_table)
+    n = ctypes.c_size_t(0)
+    check("gva_decode_workspace_size", _lib.load().gva_decode_workspace_size(
+        ctypes.byref(s), int(max_seq_len), ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(nbytes, dev, workspace):
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError("workspace too small")
+    return workspace
+
+
+def decode_attention(qa, v_pool, k_pool, block_table, seq_lens, max_seq_len,
+                     workspace=None, out=None, lse=None, want_lse=True):
+    """out[B,H,d_h] (and lse[B,H]) of the absorbed query over the paged
+    value cache and shared positional-key cache (gva_decode_attention)."""
+    dev = qa.device
+    _need(qa, "qa", torch.float32, dev, 3)
+    _need(v_pool, "v_pool", v_pool.dtype, dev, 4)
+    _need(k_pool, "k_pool", v_pool.dtype, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    B, H, dq = qa.shape
+    d_h, d_r = v_pool.shape[3], k_pool.shape[2]
+    if dq != d_h + d_r or block_table.shape[0] != B or seq_lens.shape[0] != B \
+            or k_pool.shape[:2] != v_pool.shape[:2]:
+        raise ValueError("inconsistent shapes for decode_attention")
+    s = _decode_shape(B, H, v_pool, d_r, block_table)
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    check("gva_decode_workspace_size",
+          lib.gva_decode_workspace_size(ctypes.byref(s), int(max_seq_len), ctypes.byref(n)))
+    workspace = _workspace(n.value, dev, workspace)
+    if out is None:
+        out = torch.empty((B, H, d_h), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    st = lib.gva_decode_attention(
+        ctypes.byref(s), _ptr(qa), _ptr(v_pool), _ptr(k_pool), _ptr(block_table),
+        _ptr(seq_lens), int(max_seq_len), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+        _stream(dev))
+    check("gva_decode_attention", st)
+    return out, lse
+
+
+def gqa_decode_attention(q, k_pool, v_pool, block_table, seq_lens, max_seq_len,
+                         softmax_scale=None, workspace=None, out=None, lse=None,
+                         want_lse=True):
+    """Same-shape grouped-query attention decode (gqa_decode_attention)."""
+    dev = q.device
+    _need(q, "q", torch.float32, dev, 3)
+    _need(v_pool, "v_pool", v_pool.dtype, dev, 4)
+    _need(k_pool, "k_pool", v_pool.dtype, dev, 4)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    B, H, d_h = q.shape
+    if tuple(k_pool.shape) != tuple(v_pool.shape) or v_pool.shape[3] != d_h:
+        raise ValueError("inconsistent shapes for gqa_decode_attention")
+    s = _decode_shape(B, H, v_pool, 0, block_table, True)
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    check("gqa_decode_workspace_size",
+          lib.gqa_decode_workspace_size(ctypes.byref(s), int(max_seq_len), ctypes.byref(n)))
+    workspace = _workspace(n.value, dev, workspace)
+    if out is None:
+        out = torch.empty((B, H, d_h), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    st = lib.gqa_decode_attention(
+        ctypes.byref(s), _ptr(q), float(softmax_scale or 0.0), _ptr(k_pool),
+        _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), int(max_seq_len),
+        _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(out), _ptr(lse), _stream(dev))
+    check("gqa_decode_attention", st)
+    return out, lse

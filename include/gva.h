@@ -1,0 +1,191 @@
+/*
+ * libgva -- Grouped Value Attention (GVA) absorbed decode attention on
+ * AMD Instinct MI355X (gfx950).  Plain C ABI: no HIP or torch types appear in
+ * the signatures; streams are passed as `void*` (a hipStream_t, NULL for the
+ * default stream).
+ *
+ * The method (summaries of "Grouped Value Attention: Efficient KV Caching
+ * via On-Demand Key Reconstruction"):
+ *   - The cache keeps only G grouped value rows V[T,G,d_h] per sequence and
+ *     one positional key k_rope[T,d_r] that all H query heads share
+ *     (onedev.kr review, sections "How it works" and "How it differs").
+ *   - Head h's content key is rebuilt from its group's values by a fixed map,
+ *     K_h = V_g(h) M_h, M_h of size d_h x d_n; because M_h is fixed the map
+ *     folds into the query once per token, q~_h = q_nope,h M_h^T, and the
+ *     content score is <q~_h, v_j> exactly (onedev.kr review, "How it works";
+ *     bisque.today explainer, Equation 7).
+ *   - Position goes through a separate decoupled-RoPE slice of width d_r: the
+ *     query slice is rotated to the query position and the shared key is
+ *     stored already rotated, k_rope = (x_j W_r) R_j^T (onedev.kr review,
+ *     "How it differs").
+ *
+ * Conventions shared by every entry point
+ *   Memory    All tensor pointers are DEVICE pointers to dense row-major
+ *             arrays, owned by the caller; the library allocates and frees
+ *             nothing and keeps no state between calls.  Pointers to arrays
+ *             read with vector loads (marked "16B") must be 16-byte aligned.
+ *   Streams   Every call only enqueues work on `stream` and returns; results
+ *             are ready when the stream reaches that point.
+ *   Errors    Argument errors are detected on the host before any HIP call
+ *             and return a non-zero gva_status with nothing enqueued.  A
+ *             failed kernel launch returns GVA_ERR_HIP.  Device-resident
+ *             values (sequence lengths, positions, block ids) cannot be
+ *             checked synchronously: kernels range-check them and turn an
+ *             out-of-range value into NaN outputs (decode) or a skipped
+ *             write (append) rather than an out-of-bounds access.
+ *   Layouts   Paged caches hold `num_blocks` blocks of `block_size` tokens:
+ *               v_pool [num_blocks][block_size][G][d_h]
+ *               k_pool [num_blocks][block_size][d_r]
+ *             Token j of sequence b lives in block block_table[b][j/bs],
+ *             slot j%bs.  A contiguous cache is the identity table.
+ *   Positions 0-based.  In decode the query token is the last cached token
+ *             of its sequence (position seq_lens[b]-1) and attends to itself.
+ *   Heads     Query head h reads value group g(h) = h / (H/G).
+ */
+#ifndef GVA_H
+#define GVA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GVA_ABI_VERSION 1
+
+typedef enum gva_status {
+  GVA_OK = 0,
+  GVA_ERR_NULL = 1,        /* a required pointer is NULL                    */
+  GVA_ERR_SHAPE = 2,       /* a size is non-positive or sizes disagree      */
+  GVA_ERR_UNSUPPORTED = 3, /* valid sizes this build has no kernel for      */
+  GVA_ERR_ALIGN = 4,       /* a 16B pointer is not 16-byte aligned          */
+  GVA_ERR_WORKSPACE = 5,   /* workspace smaller than the size query returns */
+  GVA_ERR_HIP = 6          /* the HIP runtime rejected a launch             */
+} gva_status;
+
+typedef enum gva_dtype {
+  GVA_F32 = 0,  /* IEEE binary32 cache                     */
+  GVA_BF16 = 1  /* bfloat16 cache (round-to-nearest-even)  */
+} gva_dtype;
+
+/* Sizes of one call.  Fields an entry point does not use are ignored.
+ * Supported: 1 <= H/G, H % G == 0; d_h in {32, 64, 128} (GQA: d_h in
+ * {32, 64, 128}); 2 <= d_r <= 64 and even; 1 <= d_n <= 256; block_size == 64;
+ * num_blocks, max_blocks >= 1. */
+typedef struct gva_shape {
+  int32_t B;           /* sequences in the batch                      */
+  int32_t H;           /* query heads                                 */
+  int32_t G;           /* value groups                                */
+  int32_t d_h;         /* value row width = absorbed content width    */
+  int32_t d_n;         /* unrotated content slice of each query head  */
+  int32_t d_r;         /* rotated position slice / shared key width   */
+  int32_t block_size;  /* tokens per cache block                      */
+  int32_t max_blocks;  /* columns of block_table                      */
+  int32_t num_blocks;  /* blocks in each pool                         */
+  int32_t cache_dtype; /* gva_dtype of v_pool and k_pool              */
+} gva_shape;
+
+/* Library ABI version (GVA_ABI_VERSION of the build). */
+int32_t gva_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* gva_status_string(int32_t status);
+
+/* Persistent cache scalars per token, G*d_h + d_r: the grouped values plus
+ * one positional key shared by all heads, not G*d_r (onedev.kr review, "How
+ * it differs": N_GVA = T*G*d_h + T*d_r).  Returns 0 for a NULL shape. */
+uint64_t gva_cache_scalars_per_token(const gva_shape* shape);
+
+/* Absorb each head's fixed key map into its query, once per query token
+ * (onedev.kr review, "How it works"; bisque.today explainer, Equation 7):
+ *
+ *   qa[b][h][e]       = s * sum_n q_nope[b][h][n] * M[h][e][n]   (e < d_h)
+ *   qa[b][h][d_h + i] = s * (R(pos[b]) q_rope[b][h])[i]           (i < d_r)
+ *
+ * R(p) rotates each adjacent pair (2i, 2i+1) by angle p * rope_base^(-2i/d_r)
+ * (angles, sines and cosines in float64).  s = softmax_scale, or
+ * 1/sqrt(d_n + d_r) when softmax_scale <= 0.
+ *   q_nope [B][H][d_n] f32, q_rope [B][H][d_r] f32, M [H][d_h][d_n] f32,
+ *   pos [B] i32 (query positions), qa [B][H][d_h + d_r] f32 (written).
+ * Uses B, H, d_h, d_n, d_r. */
+gva_status gva_absorb_query(const gva_shape* shape, const float* q_nope,
+                            const float* q_rope, const float* M,
+                            const int32_t* pos, float softmax_scale,
+                            float rope_base, float* qa, void* stream);
+
+/* Write one new token per sequence into the paged caches, before attention
+ * (onedev.kr review, "How it differs": the positional key is cached already
+ * rotated, k_rope = (x_j W_r) R_j^T):
+ *
+ *   v_pool[blk][slot][g][:] = round(v_new[b][g][:])
+ *   k_pool[blk][slot][:]    = round(R(pos[b]) k_new[b][:])
+ *
+ * with blk = block_table[b][pos[b]/block_size], slot = pos[b] % block_size,
+ * R as in gva_absorb_query (rotation in float64) and round the cache dtype's
+ * single round-to-nearest-even from the exact value.
+ *   v_new [B][G][d_h] f32, k_new [B][d_r] f32 (unrotated x_j W_r),
+ *   pos [B] i32, block_table [B][max_blocks] i32, v_pool/k_pool as above.
+ * A sequence whose pos or block id is out of range is skipped.
+ * Uses B, G, d_h, d_r, block_size, max_blocks, num_blocks, cache_dtype. */
+gva_status gva_append_cache(const gva_shape* shape, const float* v_new,
+                            const float* k_new, const int32_t* pos,
+                            const int32_t* block_table, float rope_base,
+                            void* v_pool, void* k_pool, void* stream);
+
+/* Bytes of workspace gva_decode_attention needs for these sizes and this
+ * upper bound on sequence length (split-context partial results). */
+gva_status gva_decode_workspace_size(const gva_shape* shape,
+                                     int32_t max_seq_len, size_t* bytes);
+
+/* Decode attention of the absorbed query over the value cache (onedev.kr
+ * review, "How it works": content attention reads only the value cache and
+ * builds no key tensor):
+ *
+ *   score[b][h][j] = <qa[b][h][0:d_h], V[b][j][g(h)]>
+ *                  + <qa[b][h][d_h:], k_rope[b][j]>          (j < seq_lens[b])
+ *   p = softmax_j(score);   out[b][h] = sum_j p_j V[b][j][g(h)]
+ *   lse[b][h] = log sum_j exp(score[b][h][j])
+ *
+ * The scale is already folded into qa (gva_absorb_query).  The context is
+ * split into chunks whose partial softmax states are merged by log-sum-exp;
+ * the split depends only on the sizes, so results are bitwise reproducible.
+ *   qa [B][H][d_h + d_r] f32 (16B), v_pool/k_pool (16B), block_table
+ *   [B][max_blocks] i32, seq_lens [B] i32 on the device, each
+ *   <= min(max_seq_len, max_blocks*block_size); max_seq_len (host) >= 0;
+ *   workspace of at least gva_decode_workspace_size bytes (16B; contents
+ *   undefined afterwards); out [B][H][d_h] f32 (16B); lse [B][H] f32 or NULL.
+ * seq_lens[b] == 0 gives out = 0 and lse = -inf.  Uses every shape field
+ * except d_n. */
+gva_status gva_decode_attention(const gva_shape* shape, const float* qa,
+                                const void* v_pool, const void* k_pool,
+                                const int32_t* block_table,
+                                const int32_t* seq_lens, int32_t max_seq_len,
+                                void* workspace, size_t workspace_bytes,
+                                float* out, float* lse, void* stream);
+
+/* Same-shape grouped-query attention decode, the baseline GVA is compared
+ * with: each group stores both a key and a value row per token
+ * (onedev.kr review, "What it is"; N_GQA = 2*T*G*d_h):
+ *
+ *   score[b][h][j] = s * <q[b][h], K[b][j][g(h)]>;  softmax;  out = sum p V
+ *
+ *   q [B][H][d_h] f32 (16B, position encoding already applied),
+ *   k_pool/v_pool [num_blocks][block_size][G][d_h] (16B), s = softmax_scale
+ *   or 1/sqrt(d_h) when <= 0; other arguments as gva_decode_attention.
+ * Uses B, H, G, d_h, block_size, max_blocks, num_blocks, cache_dtype. */
+gva_status gqa_decode_workspace_size(const gva_shape* shape,
+                                     int32_t max_seq_len, size_t* bytes);
+gva_status gqa_decode_attention(const gva_shape* shape, const float* q,
+                                float softmax_scale, const void* k_pool,
+                                const void* v_pool,
+                                const int32_t* block_table,
+                                const int32_t* seq_lens, int32_t max_seq_len,
+                                void* workspace, size_t workspace_bytes,
+                                float* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GVA_H */

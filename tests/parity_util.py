@@ -1,0 +1,59 @@
+"""Helpers shared by the GPU parity tests: tolerances, sub-pools for sampled
+oracle checks, and printing of the case being run (flushed before each GPU
+step so that a failing run names its case)."""
+import sys
+
+import numpy as np
+import torch
+
+
+def announce(*parts):
+    print("[case]", *parts, flush=True)
+    sys.stdout.flush()
+
+
+def rel_l2(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+
+def assert_fp32_parity(got, ref, tol=1e-5, what="out"):
+    """float32-cache bar: relative L2 error <= 1e-5."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = rel_l2(got, ref)
+    assert err <= tol, f"{what}: rel L2 {err:.3e} > {tol:.1e}"
+    return err
+
+
+def assert_bf16_parity(got, ref, frac=1e-2, what="out"):
+    """bf16-cache bar: every |error| <= 1e-2 * RMS(reference output) (this
+    implies RMS(error) <= 1e-2 * RMS(reference))."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    worst = float(np.max(np.abs(got - ref)))
+    assert worst <= frac * rms, \
+        f"{what}: max|err| {worst:.3e} > {frac:.0e} * RMS {rms:.3e}"
+    return worst / rms
+
+
+def seq_subpool(x, b, keys=("v_pool", "k_pool")):
+    """Host copies of the cache blocks of sequence b, renumbered 0..nb-1, so
+    the oracle can run on one sequence of a large pool."""
+    n = int(x["seq_lens_host"][b])
+    bs = 64
+    nb = max(1, -(-n // bs))
+    ids = x["block_table_host"][b, :nb].long()
+    dev = x[keys[0]].device
+    sub = {k: x[k][ids.to(dev)].cpu() for k in keys}
+    sub["block_table"] = np.arange(nb)[None, :]
+    sub["seq_lens"] = np.array([n])
+    return sub
+
+
+def cpu(t):
+    return t.detach().cpu()

@@ -1,0 +1,191 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point the
+header declares, and rejects bad arguments on the host before any HIP call.
+
+No test here passes a fake pointer through to a launch: every call either
+fails validation first or (on a machine with no GPU) reaches the HIP runtime,
+which refuses for lack of a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT, gpu_available
+
+HEADER = os.path.join(ROOT, "include", "gva.h")
+
+
+@pytest.fixture(scope="module")
+def g():
+    import compressed_kv_cache_amd as pkg
+    return pkg
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:gva|gqa)_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = header_functions()
+    for n in ("gva_absorb_query", "gva_append_cache", "gva_decode_attention",
+              "gva_decode_workspace_size", "gqa_decode_attention",
+              "gqa_decode_workspace_size", "gva_cache_scalars_per_token",
+              "gva_status_string", "gva_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(g):
+    lib = ctypes.CDLL(g.LIB_PATH)
+    missing = [n for n in header_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding knows every one of them
+    from compressed_kv_cache_amd._lib import SIGNATURES
+    assert sorted(SIGNATURES) == header_functions()
+
+
+def test_version_and_status_strings(g):
+    assert g.lib.gva_abi_version() == 1
+    for code in range(7):
+        assert g.lib.gva_status_string(code)
+    assert g.lib.gva_status_string(99) == b"unknown status"
+
+
+def test_cache_scalars_per_token(g):
+    assert g.cache_scalars_per_token(4, 64, 16) == 272
+    assert g.cache_scalars_per_token(4, 64, 24) == 280
+    assert g.cache_scalars_per_token(8, 128, 32) == 1056
+    assert g.lib.gva_cache_scalars_per_token(None) == 0
+
+
+def _shape(g, **kw):
+    d = dict(B=2, H=16, G=4, d_h=64, d_n=48, d_r=16, max_blocks=4,
+             num_blocks=8, cache_dtype=__import__("torch").bfloat16)
+    d.update(kw)
+    return g.make_shape(**d)
+
+
+def _ws(g, s, max_seq_len=256):
+    n = ctypes.c_size_t(0)
+    st = g.lib.gva_decode_workspace_size(ctypes.byref(s), max_seq_len, ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=15), 2),                 # H % G != 0
+    (dict(G=0), 2),
+    (dict(d_h=48), 3),               # unsupported width
+    (dict(d_r=15), 3),               # odd position slice
+    (dict(d_r=0), 2),
+    (dict(d_r=66), 3),
+    (dict(max_blocks=0), 2),
+    (dict(num_blocks=0), 2),
+    (dict(B=-1), 2),
+])
+def test_workspace_query_validates_shape(g, kw, code):
+    st, _ = _ws(g, _shape(g, **kw))
+    assert st == code
+
+
+def test_workspace_query_bounds(g):
+    s = _shape(g)
+    st, n = _ws(g, s, 256)
+    assert st == 0 and n > 0
+    assert _ws(g, s, 257)[0] == 2      # longer than max_blocks * 64
+    assert _ws(g, s, -1)[0] == 2
+    assert _ws(g, s, 0)[0] == 0
+    bad = _shape(g, cache_dtype=None)
+    bad.cache_dtype = 7
+    assert _ws(g, bad)[0] == 3
+    bs = _shape(g)
+    bs.block_size = 32
+    assert _ws(g, bs)[0] == 3
+    assert g.lib.gva_decode_workspace_size(ctypes.byref(s), 64, None) == 1
+    assert g.lib.gva_decode_workspace_size(None, 64, ctypes.byref(ctypes.c_size_t())) == 1
+
+
+def _decode(g, s, ptrs, ws_bytes=1 << 30, max_seq_len=128):
+    P = ctypes.c_void_p
+    return g.lib.gva_decode_attention(
+        ctypes.byref(s), P(ptrs.get("qa")), P(ptrs.get("v")), P(ptrs.get("k")),
+        P(ptrs.get("bt")), P(ptrs.get("sl")), max_seq_len, P(ptrs.get("ws")),
+        ws_bytes, P(ptrs.get("out")), P(ptrs.get("lse")), None)
+
+
+GOOD = dict(qa=0x10000, v=0x20000, k=0x30000, bt=0x40000, sl=0x50000,
+            ws=0x60000, out=0x70000, lse=0x80000)
+
+
+@pytest.mark.parametrize("missing", ["qa", "v", "k", "bt", "sl", "ws", "out"])
+def test_decode_null_pointers(g, missing):
+    p = dict(GOOD)
+    p[missing] = None
+    assert _decode(g, _shape(g), p) == 1
+
+
+@pytest.mark.parametrize("which", ["qa", "v", "k", "ws", "out"])
+def test_decode_alignment(g, which):
+    p = dict(GOOD)
+    p[which] += 8
+    assert _decode(g, _shape(g), p) == 4
+
+
+def test_decode_workspace_too_small(g):
+    s = _shape(g)
+    _, need = _ws(g, s, 128)
+    assert _decode(g, s, GOOD, ws_bytes=need - 1) == 5
+
+
+def test_decode_empty_batch_is_noop(g):
+    s = _shape(g, B=0)
+    assert _decode(g, s, {}) == 0
+
+
+def test_absorb_validation(g):
+    P = ctypes.c_void_p
+    s = _shape(g)
+    args = [P(0x10000)] * 4
+    f = g.lib.gva_absorb_query
+    assert f(ctypes.byref(s), *args, 0.0, 10000.0, P(None), None) == 1
+    assert f(ctypes.byref(s), *args, 0.0, -1.0, P(0x10000), None) == 2
+    assert f(ctypes.byref(s), *args, float("nan"), 1e4, P(0x10000), None) == 2
+    s2 = _shape(g, d_n=0)
+    assert f(ctypes.byref(s2), *args, 0.0, 1e4, P(0x10000), None) == 2
+    s3 = _shape(g, d_r=7)
+    assert f(ctypes.byref(s3), *args, 0.0, 1e4, P(0x10000), None) == 3
+    assert f(None, *args, 0.0, 1e4, P(0x10000), None) == 1
+
+
+def test_append_validation(g):
+    P = ctypes.c_void_p
+    f = g.lib.gva_append_cache
+    s = _shape(g)
+    ptr = [P(0x10000)] * 4
+    assert f(ctypes.byref(s), *ptr, 1e4, P(None), P(0x1000), None) == 1
+    s2 = _shape(g, G=3)
+    assert f(ctypes.byref(s2), *ptr, 1e4, P(0x1000), P(0x1000), None) == 2
+    assert f(ctypes.byref(s), *ptr, 0.0, P(0x1000), P(0x1000), None) == 2
+
+
+def test_gqa_validation(g):
+    P = ctypes.c_void_p
+    s = _shape(g)
+    n = ctypes.c_size_t()
+    assert g.lib.gqa_decode_workspace_size(ctypes.byref(s), 128, ctypes.byref(n)) == 0
+    assert n.value > 0
+    st = g.lib.gqa_decode_attention(
+        ctypes.byref(s), P(None), 0.0, P(0x1000), P(0x1000), P(0x1000), P(0x1000),
+        128, P(0x1000), n.value, P(0x1000), P(None), None)
+    assert st == 1
+
+
+@pytest.mark.skipif(gpu_available(), reason="only meaningful with no GPU present")
+def test_launch_without_device_reports_hip_error(g):
+    """With valid arguments and no GPU the HIP runtime refuses the launch."""
+    P = ctypes.c_void_p
+    s = _shape(g)
+    st = g.lib.gva_absorb_query(ctypes.byref(s), P(0x10000), P(0x10000), P(0x10000),
+                                P(0x10000), 0.0, 1e4, P(0x10000), None)
+    assert st == 6

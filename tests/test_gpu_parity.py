@@ -1,0 +1,310 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Every workload is checked end to end -- append (where the workload has it),
+absorb, decode -- against the oracle that materialises K_h = V_g(h) M_h.
+Small workloads are compared in full; the large ones in full on the GPU and
+on sampled (sequence, head) pairs for the oracle, in the same launch
+configuration the benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as o
+import synthetic as syn
+from parity_util import (announce, assert_bf16_parity, assert_fp32_parity, cpu,
+                         seq_subpool)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g(gpu):
+    import compressed_kv_cache_amd as pkg
+    return pkg
+
+
+def run_step(g, x, cfg):
+    """append (if any) -> absorb -> decode on the GPU; returns (qa, out, lse)."""
+    if cfg.append:
+        g.append_cache(x["v_new"], x["k_new"], x["pos"], x["block_table"],
+                       x["v_pool"], x["k_pool"], rope_base=cfg.rope_base)
+    qa = g.absorb_query(x["q_nope"], x["q_rope"], x["M"], x["pos"],
+                        rope_base=cfg.rope_base)
+    out, lse = g.decode_attention(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                  x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    return qa, out, lse
+
+
+def oracle_pools(x, cfg):
+    """The caches the oracle attends over (after its own append)."""
+    if not cfg.append:
+        return x["v_pool"], x["k_pool"]
+    return o.append_token(x["v_pool"], x["k_pool"], x["v_new"], x["k_new"],
+                          x["pos_host"], x["block_table_host"], base=cfg.rope_base,
+                          cache_dtype=cfg.cache_dtype)
+
+
+def gen(cfg, dev, **kw):
+    x = syn.make_gva_inputs(cfg, device=dev, **kw)
+    x["pos_host"] = cpu(x["pos"])
+    host = {k: cpu(v) for k, v in x.items() if isinstance(v, torch.Tensor)}
+    return x, host
+
+
+# ----------------------------------------------------------- tiny fp32 ----
+
+def test_tiny_fp32_end_to_end(g, gpu):
+    cfg = syn.get_config("tiny_fp32")
+    announce("tiny_fp32 end to end")
+    x, h = gen(cfg, gpu)
+    qa, out, lse = run_step(g, x, cfg)
+    ref_out, ref_lse = o.gva_decode_materialized(
+        h["q_nope"], h["q_rope"], h["M"], h["v_pool"], h["k_pool"],
+        h["block_table"], h["seq_lens"], base=cfg.rope_base)
+    ref_qa = o.absorb_query(h["q_nope"], h["q_rope"], h["M"], h["pos"])
+    assert_fp32_parity(cpu(qa), ref_qa, tol=1e-6, what="qa")
+    assert_fp32_parity(cpu(out), ref_out, what="out")
+    assert_fp32_parity(cpu(lse), ref_lse, what="lse")
+
+
+# ------------------------------------------------------ bf16 workloads ----
+
+def _check_all(g, gpu, cfg, seqs=None, heads=None, **kw):
+    x, h = gen(cfg, gpu, **kw)
+    announce(cfg.name, "B", cfg.B, "lens", x["seq_lens_host"][:8].tolist())
+    qa, out, lse = run_step(g, x, cfg)
+    vp, kp = oracle_pools(h, cfg)
+    ref_out, ref_lse = o.gva_decode_materialized(
+        h["q_nope"], h["q_rope"], h["M"], vp, kp, h["block_table"],
+        h["seq_lens"], base=cfg.rope_base, seqs=seqs, heads=heads)
+    sel = np.isfinite(ref_lse)
+    got = cpu(out).double().numpy()
+    assert_bf16_parity(got[sel], ref_out[sel], what=cfg.name + " out")
+    np.testing.assert_allclose(cpu(lse).double().numpy()[sel], ref_lse[sel],
+                               rtol=0, atol=1e-3)
+    return x, h, out
+
+
+def test_decode_350m_full(g, gpu):
+    _check_all(g, gpu, syn.get_config("decode_350m"))
+
+
+def test_wide_rope_append_full(g, gpu):
+    cfg = syn.get_config("wide_rope_append")
+    x, h, _ = _check_all(g, gpu, cfg)
+    # appended slots, bit for bit against the oracle's own append
+    vp, kp = o.append_token(h["v_pool"], h["k_pool"], h["v_new"], h["k_new"],
+                            h["pos"], h["block_table"], base=cfg.rope_base,
+                            cache_dtype="bfloat16")
+    for b in range(cfg.B):
+        p = int(h["pos"][b])
+        blk = int(h["block_table"][b, p // 64])
+        gv = cpu(x["v_pool"][blk, p % 64]).double().numpy()
+        gk = cpu(x["k_pool"][blk, p % 64]).double().numpy()
+        np.testing.assert_array_equal(gv, vp[blk, p % 64])
+        np.testing.assert_array_equal(gk, kp[blk, p % 64])
+
+
+def test_long_ragged_sampled_heads(g, gpu):
+    cfg = syn.get_config("long_ragged")
+    _check_all(g, gpu, cfg, heads=[0, 7, 15])
+
+
+def test_large_model_sampled(g, gpu):
+    cfg = syn.get_config("large_model")
+    announce("large_model generate")
+    x = syn.make_gva_inputs(cfg, device=gpu)
+    announce("large_model run")
+    qa, out, lse = run_step(g, x, cfg)
+    qh, qrh, Mh = cpu(x["q_nope"]), cpu(x["q_rope"]), cpu(x["M"])
+    pairs = [(0, 0), (37, 13), (127, 31), (64, 4)]
+    for b, hh in pairs:
+        sub = seq_subpool(x, b)
+        ref, ref_lse = o.gva_decode_materialized(
+            qh[b:b + 1], qrh[b:b + 1], Mh, sub["v_pool"], sub["k_pool"],
+            sub["block_table"], sub["seq_lens"], base=cfg.rope_base, heads=[hh])
+        assert_bf16_parity(cpu(out[b, hh]).double().numpy(), ref[0, hh],
+                           what=f"large_model b={b} h={hh}")
+        assert abs(float(lse[b, hh]) - ref_lse[0, hh]) < 1e-3
+
+
+# ----------------------------------------------------------- edge cases ----
+
+EDGE_LENS = [1, 2, 63, 64, 65, 127, 128, 129, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+@pytest.mark.parametrize("shape", [
+    # (H, G, d_h, d_n, d_r)
+    (16, 4, 64, 48, 16),
+    (8, 8, 32, 24, 8),
+    (4, 1, 128, 96, 32),
+    (32, 8, 128, 96, 32),
+    (16, 4, 64, 40, 24),
+    (16, 2, 64, 62, 2),
+])
+def test_ragged_edges(g, gpu, shape, dtype):
+    H, G, d_h, d_n, d_r = shape
+    base = syn.get_config("long_ragged")
+    cfg = syn.with_overrides(base, B=len(EDGE_LENS), H=H, G=G, d_h=d_h, d_n=d_n,
+                             d_r=d_r, cache_dtype=dtype, len_range=None, T=None)
+    lens = torch.tensor(EDGE_LENS, dtype=torch.int32)
+    x, h = gen(cfg, gpu, seq_lens=lens, shuffled=True)
+    announce("ragged edges", shape, dtype)
+    qa, out, lse = run_step(g, x, cfg)
+    ref, ref_lse = o.gva_decode_materialized(
+        h["q_nope"], h["q_rope"], h["M"], h["v_pool"], h["k_pool"],
+        h["block_table"], h["seq_lens"], base=cfg.rope_base)
+    if dtype == "float32":
+        assert_fp32_parity(cpu(out), ref)
+        assert_fp32_parity(cpu(lse), ref_lse)
+    else:
+        assert_bf16_parity(cpu(out).double().numpy(), ref)
+        np.testing.assert_allclose(cpu(lse).double().numpy(), ref_lse, atol=1e-3)
+
+
+def test_zero_length_and_slack_max_seq_len(g, gpu):
+    cfg = syn.with_overrides(syn.get_config("decode_350m"), B=4, T=None)
+    lens = torch.tensor([0, 5, 0, 300], dtype=torch.int32)
+    x, h = gen(cfg, gpu, seq_lens=lens)
+    qa = g.absorb_query(x["q_nope"], x["q_rope"], x["M"], x["pos"])
+    # max_seq_len larger than any length: the extra chunks are empty
+    mx = 64 * x["block_table"].shape[1]
+    out, lse = g.decode_attention(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                  x["seq_lens"], mx)
+    torch.cuda.synchronize()
+    o_ = cpu(out).double().numpy()
+    l_ = cpu(lse).double().numpy()
+    assert np.all(o_[0] == 0) and np.all(o_[2] == 0)
+    assert np.all(l_[0] == -np.inf) and np.all(l_[2] == -np.inf)
+    ref, ref_lse = o.gva_decode_materialized(
+        h["q_nope"], h["q_rope"], h["M"], h["v_pool"], h["k_pool"],
+        h["block_table"], h["seq_lens"], seqs=[1, 3])
+    assert_bf16_parity(o_[[1, 3]], ref[[1, 3]])
+
+
+def test_out_of_range_device_values_give_nan(g, gpu):
+    """A length beyond max_seq_len or a block id beyond the pool is reported as
+    NaN output for that sequence; the others are unaffected."""
+    cfg = syn.with_overrides(syn.get_config("decode_350m"), B=3, T=128)
+    x, h = gen(cfg, gpu)
+    qa = g.absorb_query(x["q_nope"], x["q_rope"], x["M"], x["pos"])
+    bt = x["block_table"].clone()
+    bt[1, 1] = x["num_blocks"] + 5       # block id past the pool
+    sl = x["seq_lens"].clone()
+    sl[2] = 10_000                       # longer than max_seq_len
+    out, lse = g.decode_attention(qa, x["v_pool"], x["k_pool"], bt, sl, 128)
+    torch.cuda.synchronize()
+    o_ = cpu(out)
+    assert torch.isnan(o_[1]).all() and torch.isnan(o_[2]).all()
+    assert torch.isfinite(o_[0]).all()
+
+
+# ------------------------------------------------------------ properties ----
+
+def test_constant_values_give_constant_output(g, gpu):
+    cfg = syn.with_overrides(syn.get_config("decode_350m"), B=2, T=777)
+    x, _ = gen(cfg, gpu)
+    nb = x["num_blocks"]
+    x["v_pool"].fill_(1.0)
+    qa = g.absorb_query(x["q_nope"], x["q_rope"], x["M"], x["pos"])
+    out, _ = g.decode_attention(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(cpu(out).numpy(), 1.0, rtol=0, atol=1e-6)
+
+
+def test_zero_query_gives_mean_of_values(g, gpu):
+    cfg = syn.with_overrides(syn.get_config("decode_350m"), B=2, T=500)
+    x, h = gen(cfg, gpu)
+    qa = torch.zeros((cfg.B, cfg.H, cfg.d_h + cfg.d_r), device=gpu)
+    out, lse = g.decode_attention(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                  x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    for b in range(cfg.B):
+        sub = seq_subpool(x, b)
+        V = o.gather_tokens(o.to_f64(sub["v_pool"]), sub["block_table"][0], 500, 64)
+        for hh in range(cfg.H):
+            ref = V[:, hh // 4].mean(0)
+            np.testing.assert_allclose(cpu(out[b, hh]).numpy(), ref, atol=1e-5)
+        np.testing.assert_allclose(cpu(lse[b]).numpy(), math.log(500), atol=1e-5)
+
+
+def test_bitwise_deterministic(g, gpu):
+    cfg = syn.with_overrides(syn.get_config("long_ragged"), len_range=(100, 5000))
+    x, _ = gen(cfg, gpu)
+    qa = g.absorb_query(x["q_nope"], x["q_rope"], x["M"], x["pos"])
+    a, la = g.decode_attention(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                               x["seq_lens"], x["max_seq_len"])
+    b, lb = g.decode_attention(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                               x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_paged_shuffled_equals_contiguous(g, gpu):
+    """The same token rows reached through a shuffled table or through the
+    identity table give bit-identical results."""
+    cfg = syn.with_overrides(syn.get_config("long_ragged"), len_range=(300, 3000))
+    x, h = gen(cfg, gpu)
+    qa = g.absorb_query(x["q_nope"], x["q_rope"], x["M"], x["pos"])
+    a, _ = g.decode_attention(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                              x["seq_lens"], x["max_seq_len"])
+    # lay the same rows out contiguously: block i of seq b -> slot order
+    lens = x["seq_lens_host"].tolist()
+    nbs = [-(-n // 64) for n in lens]
+    ids = torch.cat([x["block_table_host"][b, :nbs[b]] for b in range(cfg.B)]).long()
+    vp = x["v_pool"][ids.to(gpu)].contiguous()
+    kp = x["k_pool"][ids.to(gpu)].contiguous()
+    table = torch.zeros_like(x["block_table_host"])
+    off = 0
+    for b, nb in enumerate(nbs):
+        table[b, :nb] = torch.arange(off, off + nb)
+        off += nb
+    b_, _ = g.decode_attention(qa, vp, kp, table.to(gpu), x["seq_lens"],
+                               x["max_seq_len"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b_)
+
+
+# -------------------------------------------------------------------- GQA ----
+
+@pytest.mark.parametrize("name,sample", [("decode_350m", None),
+                                         ("large_model", [(0, 0), (99, 30)])])
+def test_gqa_decode(g, gpu, name, sample):
+    cfg = syn.get_config(name)
+    announce("gqa", name)
+    x = syn.make_gqa_inputs(cfg, device=gpu)
+    out, lse = g.gqa_decode_attention(x["q"], x["k_pool"], x["v_pool"],
+                                      x["block_table"], x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    if sample is None:
+        h = {k: cpu(v) for k, v in x.items() if isinstance(v, torch.Tensor)}
+        ref, ref_lse = o.gqa_decode(h["q"], h["k_pool"], h["v_pool"], h["block_table"],
+                                    h["seq_lens"])
+        assert_bf16_parity(cpu(out).double().numpy(), ref, what="gqa out")
+        np.testing.assert_allclose(cpu(lse).double().numpy(), ref_lse, atol=1e-3)
+    else:
+        qh = cpu(x["q"])
+        for b, hh in sample:
+            sub = seq_subpool(x, b)
+            ref, _ = o.gqa_decode(qh[b:b + 1], sub["k_pool"], sub["v_pool"],
+                                  sub["block_table"], sub["seq_lens"], heads=[hh])
+            assert_bf16_parity(cpu(out[b, hh]).double().numpy(), ref[0, hh])
+
+
+def test_gqa_small_fp32(g, gpu):
+    cfg = syn.with_overrides(syn.get_config("tiny_fp32"), B=3, T=None,
+                             len_range=(1, 300), shuffled_blocks=True)
+    x = syn.make_gqa_inputs(cfg, device=gpu)
+    out, lse = g.gqa_decode_attention(x["q"], x["k_pool"], x["v_pool"],
+                                      x["block_table"], x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    h = {k: cpu(v) for k, v in x.items() if isinstance(v, torch.Tensor)}
+    ref, ref_lse = o.gqa_decode(h["q"], h["k_pool"], h["v_pool"], h["block_table"],
+                                h["seq_lens"])
+    assert_fp32_parity(cpu(out), ref)
