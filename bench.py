@@ -99,53 +99,94 @@ def main():
     pools = [(x["v_pool"], x["k_pool"])]
     for _ in range(R - 1):
         pools.append((x["v_pool"].clone(), x["k_pool"].clone()))
-    ws = torch.empty(gva.decode_workspace_bytes(cfg.B, cfg.H, x["v_pool"], x["k_pool"],
+    ws = torch.zeros(gva.decode_workspace_bytes(cfg.B, cfg.H, x["v_pool"], x["k_pool"],
                                                 x["block_table"], x["max_seq_len"]),
                      dtype=torch.uint8, device=dev)
+    ws_step = torch.zeros(gva.decode_step_workspace_bytes(x["q_nope"], x["q_rope"], x["v_pool"],
+                                                          x["k_pool"], x["block_table"],
+                                                          x["max_seq_len"]),
+                          dtype=torch.uint8, device=dev)
     qa = torch.empty((cfg.B, cfg.H, cfg.d_h + cfg.d_r), dtype=torch.float32, device=dev)
     out = torch.empty((cfg.B, cfg.H, cfg.d_h), dtype=torch.float32, device=dev)
     lse = torch.empty((cfg.B, cfg.H), dtype=torch.float32, device=dev)
 
-    def step(i, ev=None):
+    def step(i):
+        # append + absorb + decode: gva_decode_step, two launches
         vp, kp = pools[i % R]
-        gva.append_cache(x["v_new"], x["k_new"], x["pos"], x["block_table"], vp, kp,
-                         rope_base=cfg.rope_base)
-        gva.absorb_query(x["q_nope"], x["q_rope"], x["M"], x["pos"],
-                         rope_base=cfg.rope_base, out=qa)
-        if ev is not None:
-            ev[0].record()
+        gva.decode_step(x["q_nope"], x["q_rope"], x["M"], vp, kp, x["block_table"],
+                        x["seq_lens"], x["max_seq_len"], v_new=x["v_new"], k_new=x["k_new"],
+                        rope_base=cfg.rope_base, workspace=ws_step, out=out, lse=lse)
+
+    gva.absorb_query(x["q_nope"], x["q_rope"], x["M"], x["pos"], rope_base=cfg.rope_base,
+                     out=qa)
+
+    def decode_only(i):
+        vp, kp = pools[i % R]
         gva.decode_attention(qa, vp, kp, x["block_table"], x["seq_lens"],
                              x["max_seq_len"], workspace=ws, out=out, lse=lse)
-        if ev is not None:
-            ev[1].record()
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # whole steps, one event pair around K steps
+    # eager: steps issued one by one from Python (launch overhead included)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record()
     for i in range(args.steps):
         step(i)
     t1.record()
     torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+    eager_ms = t0.elapsed_time(t1) / args.steps
+    eager_out = out.clone()
 
-    # decode launches alone, an event pair around each launch
+    # HIP graphs of R consecutive steps (one per rotating cache copy), and of
+    # R decode launches alone; replayed back to back.
+    g_step, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(R):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g_step):
+        for i in range(R):
+            step(i)
+    with torch.cuda.graph(g_dec):
+        for i in range(R):
+            decode_only(i)
+    torch.cuda.synchronize()
+    g_step.replay()
+    torch.cuda.synchronize()
+    graph_matches_eager = bool(torch.equal(out, eager_out))
+    reps = max(1, -(-args.steps // R))
+    for _ in range(2):
+        g_step.replay()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(reps):
+        g_step.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / (reps * R)
+    steps_timed = reps * R
+
+    # decode launches alone: one event pair per graph of R launches
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+           for _ in range(reps)]
+    g_dec.replay()
     torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, evs[i])
+    for i in range(reps):
+        evs[i][0].record()
+        g_dec.replay()
+        evs[i][1].record()
     torch.cuda.synchronize()
-    dec_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    dec_ms = sorted(a.elapsed_time(b) / R for a, b in evs)
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
     dec_med_ms = dec_ms[len(dec_ms) // 2]
-    print(f"[bench] step {ms_per_step * 1e3:.2f} us, decode avg {dec_avg_ms * 1e3:.2f} us",
+    print(f"[bench] step {ms_per_step * 1e3:.2f} us (eager {eager_ms * 1e3:.2f} us), "
+          f"decode avg {dec_avg_ms * 1e3:.2f} us, graph==eager {graph_matches_eager}",
           file=sys.stderr, flush=True)
 
     value = cache_bytes / (ms_per_step * 1e-3) / 1e9
@@ -165,6 +206,8 @@ def main():
         "queries_ctx_per_s": tokens / (ms_per_step * 1e-3),
         "head_queries_ctx_per_s": cfg.H * tokens / (ms_per_step * 1e-3),
         "pct_of_hbm_peak": 100.0 * value / PEAK_HBM_GBS,
+        "eager_ms_per_step": eager_ms,
+        "graph_replay_matches_eager": graph_matches_eager,
         "decode_us_avg": dec_avg_ms * 1e3,
         "decode_us_median": dec_med_ms * 1e3,
         "decode_GBps": achieved,
@@ -185,7 +228,7 @@ def main():
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps_timed,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
@@ -199,7 +242,9 @@ def main():
             "T": cfg.T if cfg.T else "ragged",
             "context_tokens": tokens, "cache_dtype": cfg.cache_dtype,
             "accumulate": "f32",
-            "step": "append+absorb+decode(split+merge)",
+            "step": "gva_decode_step: append+absorb (1 launch) + decode with in-kernel merge "
+                    "(1 launch)",
+            "timing": "HIP graph of R steps replayed back to back",
             "rotating_cache_copies": R,
         },
         "roofline": {
@@ -227,22 +272,33 @@ def bench_gqa(torch, gva, syn, cfg, dev, steps, warmup):
         (y["k_pool"].clone(), y["v_pool"].clone()) for _ in range(R - 1)]
     out = torch.empty((cfg.B, cfg.H, cfg.d_h), dtype=torch.float32, device=dev)
     lse = torch.empty((cfg.B, cfg.H), dtype=torch.float32, device=dev)
-    for i in range(warmup):
+    ws = torch.zeros(max(16, gva.gqa_decode_workspace_bytes(
+        cfg.B, cfg.H, y["k_pool"], y["v_pool"], y["block_table"], y["max_seq_len"])),
+        dtype=torch.uint8, device=dev)
+
+    def launch(i):
         kp, vp = pools[i % R]
         gva.gqa_decode_attention(y["q"], kp, vp, y["block_table"], y["seq_lens"],
-                                 y["max_seq_len"], out=out, lse=lse)
+                                 y["max_seq_len"], workspace=ws, out=out, lse=lse)
+
+    for i in range(max(warmup, R)):
+        launch(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for i in range(steps):
-        kp, vp = pools[i % R]
-        evs[i][0].record()
-        gva.gqa_decode_attention(y["q"], kp, vp, y["block_table"], y["seq_lens"],
-                                 y["max_seq_len"], out=out, lse=lse)
-        evs[i][1].record()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(R):
+            launch(i)
+    g.replay()
     torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in evs]
-    avg = sum(ms) / len(ms)
+    reps = max(1, -(-steps // R))
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    avg = t0.elapsed_time(t1) / (reps * R)
     del pools, y
     torch.cuda.empty_cache()
     return {"us_avg": avg * 1e3, "cache_bytes": byts, "GBps": byts / (avg * 1e-3) / 1e9}

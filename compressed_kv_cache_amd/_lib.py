@@ -37,6 +37,9 @@ SIGNATURES = {
     "gva_decode_workspace_size": (_I32, [_SHAPE, _I32, ctypes.POINTER(_SIZE)]),
     "gva_decode_attention": (_I32, [_SHAPE, _P, _P, _P, _P, _P, _I32, _P, _SIZE,
                                     _P, _P, _P]),
+    "gva_decode_step_workspace_size": (_I32, [_SHAPE, _I32, ctypes.POINTER(_SIZE)]),
+    "gva_decode_step": (_I32, [_SHAPE, _P, _P, _P, _F32, _F32, _P, _P, _P, _P, _P, _P, _I32,
+                               _P, _SIZE, _P, _P, _P]),
     "gqa_decode_workspace_size": (_I32, [_SHAPE, _I32, ctypes.POINTER(_SIZE)]),
     "gqa_decode_attention": (_I32, [_SHAPE, _P, _F32, _P, _P, _P, _P, _I32, _P,
                                     _SIZE, _P, _P, _P]),
@@ -54,7 +57,7 @@ def load(path=None):
     if not os.path.exists(p):
         raise ImportError(
             f"libgva.so not found at {p}; build it with "
-            "`python -m compressed_kv_cache_amd.build` (hipcc, gfx950)")
+            "`python compressed_kv_cache_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(p)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

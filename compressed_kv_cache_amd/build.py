@@ -1,6 +1,7 @@
 """Build libgva.so (HIP for gfx950) in-tree with hipcc.
 
-Usage: python -m compressed_kv_cache_amd.build  [--verbose]
+Usage: python compressed_kv_cache_amd/build.py [--verbose]
+(run by path: importing the package loads the library this script builds)
 """
 import os
 import shutil

@@ -48,6 +48,27 @@ gva_status check_rope_width(int d_r) {
 
 gva_status to_status(hipError_t e) { return e == hipSuccess ? GVA_OK : GVA_ERR_HIP; }
 
+gva_status check_absorb_shape(const gva_shape& s, float softmax_scale, float rope_base) {
+  if (s.B < 0 || s.H < 1 || s.d_n < 1) return GVA_ERR_SHAPE;
+  if (!dh_ok(s.d_h)) return GVA_ERR_UNSUPPORTED;
+  if (s.d_n > 256) return GVA_ERR_UNSUPPORTED;
+  gva_status st = check_rope_width(s.d_r);
+  if (st != GVA_OK) return st;
+  if (!(rope_base > 0.f) || !isfinite(rope_base)) return GVA_ERR_SHAPE;
+  if (!isfinite(softmax_scale)) return GVA_ERR_SHAPE;
+  return GVA_OK;
+}
+
+float absorb_scale(const gva_shape& s, float softmax_scale) {
+  return softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(s.d_n + s.d_r));
+}
+
+// Fused step workspace: [decode workspace, padded to 256 B][qa].
+size_t step_qa_offset(size_t decode_bytes) { return ((decode_bytes + 255) / 256) * 256; }
+size_t step_qa_bytes(const gva_shape& s) {
+  return static_cast<size_t>(s.B) * s.H * (s.d_h + s.d_r) * sizeof(float);
+}
+
 int round_up(long long x, int m) { return static_cast<int>(((x + m - 1) / m) * m); }
 
 gva::DecodePlan plan_ref(const gva_shape& s, int max_seq_len) {
@@ -58,8 +79,9 @@ gva::DecodePlan plan_ref(const gva_shape& s, int max_seq_len) {
   if (chunk < kBlockSize) chunk = kBlockSize;
   p.chunk_tokens = chunk;
   p.num_chunks = max_seq_len > 0 ? (max_seq_len + chunk - 1) / chunk : 1;
-  p.partial_floats = static_cast<size_t>(s.B) * p.num_chunks * s.H * (s.d_h + 2);
-  p.workspace_bytes = p.partial_floats * sizeof(float);
+  p.partial_floats = static_cast<size_t>(s.B) * p.num_chunks * s.H * (s.d_h + 4);
+  p.ticket_bytes = gva::ticket_bytes(s.B);
+  p.workspace_bytes = p.ticket_bytes + p.partial_floats * sizeof(float);
   return p;
 }
 
@@ -134,7 +156,8 @@ gva_status decode(const gva_shape* shape, const float* q, float q_scale, const v
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.max_seq_len = max_seq_len;
-  a.partials = static_cast<float*>(workspace);
+  a.tickets = static_cast<unsigned*>(workspace);
+  a.partials = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + plan.ticket_bytes);
   a.out = out;
   a.lse = lse;
   a.q_scale = q_scale;
@@ -174,19 +197,12 @@ gva_status gva_absorb_query(const gva_shape* shape, const float* q_nope, const f
                             float rope_base, float* qa, void* stream) {
   if (!shape) return GVA_ERR_NULL;
   const gva_shape& s = *shape;
-  if (s.B < 0 || s.H < 1 || s.d_n < 1) return GVA_ERR_SHAPE;
-  if (!dh_ok(s.d_h)) return GVA_ERR_UNSUPPORTED;
-  if (s.d_n > 256) return GVA_ERR_UNSUPPORTED;
-  gva_status st = check_rope_width(s.d_r);
+  gva_status st = check_absorb_shape(s, softmax_scale, rope_base);
   if (st != GVA_OK) return st;
-  if (!(rope_base > 0.f) || !isfinite(rope_base)) return GVA_ERR_SHAPE;
-  if (!isfinite(softmax_scale)) return GVA_ERR_SHAPE;
   if (s.B == 0) return GVA_OK;
   if (!q_nope || !q_rope || !M || !pos || !qa) return GVA_ERR_NULL;
-  const float scale = softmax_scale > 0.f ? softmax_scale
-                                          : 1.0f / sqrtf(static_cast<float>(s.d_n + s.d_r));
-  return to_status(gva::launch_absorb(s, q_nope, q_rope, M, pos, scale, rope_base, qa,
-                                      static_cast<hipStream_t>(stream)));
+  return to_status(gva::launch_absorb(s, q_nope, q_rope, M, pos, absorb_scale(s, softmax_scale),
+                                      rope_base, qa, static_cast<hipStream_t>(stream)));
 }
 
 gva_status gva_append_cache(const gva_shape* shape, const float* v_new, const float* k_new,
@@ -216,6 +232,64 @@ gva_status gva_decode_attention(const gva_shape* shape, const float* qa, const v
                                 size_t workspace_bytes, float* out, float* lse, void* stream) {
   return decode(shape, qa, 1.0f, k_pool, v_pool, block_table, seq_lens, max_seq_len, workspace,
                 workspace_bytes, out, lse, stream, false);
+}
+
+gva_status gva_decode_step_workspace_size(const gva_shape* shape, int32_t max_seq_len,
+                                          size_t* bytes) {
+  if (!bytes) return GVA_ERR_NULL;
+  size_t dec = 0;
+  gva_status st = workspace_size(shape, max_seq_len, false, &dec);
+  if (st != GVA_OK) return st;
+  *bytes = step_qa_offset(dec) + step_qa_bytes(*shape);
+  return GVA_OK;
+}
+
+gva_status gva_decode_step(const gva_shape* shape, const float* q_nope, const float* q_rope,
+                           const float* M, float softmax_scale, float rope_base,
+                           const float* v_new, const float* k_new, void* v_pool, void* k_pool,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                           float* out, float* lse, void* stream) {
+  if (!shape) return GVA_ERR_NULL;
+  const gva_shape& s = *shape;
+  gva_status st = check_absorb_shape(s, softmax_scale, rope_base);
+  if (st != GVA_OK) return st;
+  st = check_decode_args(shape, max_seq_len, false);
+  if (st != GVA_OK) return st;
+  gva::DecodePlan plan;
+  st = make_plan(s, max_seq_len, false, &plan);
+  if (st != GVA_OK) return st;
+  if (s.B == 0) return GVA_OK;
+  if (!q_nope || !q_rope || !M || !v_pool || !k_pool || !block_table || !seq_lens || !out ||
+      !workspace)
+    return GVA_ERR_NULL;
+  if ((v_new == nullptr) != (k_new == nullptr)) return GVA_ERR_NULL;
+  if (!aligned16(v_pool) || !aligned16(k_pool) || !aligned16(out) || !aligned16(workspace))
+    return GVA_ERR_ALIGN;
+  const size_t qa_off = step_qa_offset(plan.workspace_bytes);
+  if (workspace_bytes < qa_off + step_qa_bytes(s)) return GVA_ERR_WORKSPACE;
+  float* qa = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + qa_off);
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  // append (optional) + absorb in one launch; query position = seq_lens[b] - 1
+  hipError_t e = gva::launch_prologue(s, q_nope, q_rope, M, absorb_scale(s, softmax_scale), qa,
+                                      v_new, k_new, block_table, v_pool, k_pool, seq_lens, -1,
+                                      rope_base, strm);
+  if (e != hipSuccess) return GVA_ERR_HIP;
+  gva::DecodeArgs a{};
+  a.q = qa;
+  a.v_pool = v_pool;
+  a.k_pool = k_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.max_seq_len = max_seq_len;
+  a.tickets = static_cast<unsigned*>(workspace);
+  a.partials = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + plan.ticket_bytes);
+  a.out = out;
+  a.lse = lse;
+  a.q_scale = 1.0f;
+  a.keys_separate = false;
+  if (plan.kernel == gva::kKernelMfma) return to_status(gva::launch_decode_mfma(s, plan, a, strm));
+  return to_status(gva::launch_decode_ref(s, plan, a, strm));
 }
 
 gva_status gqa_decode_workspace_size(const gva_shape* shape, int32_t max_seq_len,

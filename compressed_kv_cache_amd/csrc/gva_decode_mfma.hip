@@ -1,17 +1,671 @@
-// Matrix-core decode kernel (bf16 caches).  Placeholder until the kernel
-// lands: no shape is routed here yet.
+// Split-context decode attention on the gfx950 matrix cores (bf16 caches).
+//
+// The decode scan is bound by HBM bandwidth: every cached byte is read once
+// and used for ~8.5 flops.  Plain fp32 FMAs would be a co-bound at that
+// intensity, so both contractions run on MFMA and the vector ALUs only do
+// the online softmax.  Query and softmax weights are split into bf16 hi + lo
+// parts so the products carry ~16 mantissa bits; the cache values themselves
+// are exact bf16.
+//
+// Work split: block (c, b) owns chunk c of sequence b and runs 4 waves.
+// Query heads come in tiles of 16 (one MFMA column each); a head tile covers
+// GT = 16/(H/G) whole value groups.  With H/16 head tiles the waves are
+// divided between head tiles, and the waves of a head tile take the chunk's
+// 16-token tiles in turn.  A wave handles its tiles two at a time:
+//   1. each tile's value rows of its groups (and k_rope rows) come from HBM
+//      straight into MFMA A-operand registers (16 B per lane per k-step);
+//      three register sets rotate, so two tiles are in flight while one is
+//      consumed;
+//   2. scores S^T[token][head] = V_g . qa^T per group (16x16x32 MFMAs) plus
+//      k_rope . qr^T (16x16x16), keeping for each head its own group's sum;
+//   3. the tile's value rows go to a wave-private LDS tile (XOR-swizzled
+//      rows, conflict-free for the row writes and the transpose reads);
+//   4. the running max/sum of each head absorb the pair's 32 scores (log2
+//      units); the max is raised only when a score exceeds it by 2^8, so the
+//      accumulator is rarely rescaled;
+//   5. out^T[dim][head] += V_g^T P^T over the pair's 32 tokens (16x16x32
+//      MFMAs), the V^T operand read with the LDS transpose load and the
+//      weights reused in place from the score registers (same lane layout).
+// The waves' states are merged in LDS into one partial record per (sequence,
+// chunk, head).  Each block then takes a ticket from its sequence's counter;
+// the block that finishes last merges the chunk records of that sequence
+// into the output (log-sum-exp) and resets the counter, so the whole decode
+// is one launch.
 #include "gva_device.h"
 #include "gva_internal.h"
 
 namespace gva {
 
-bool mfma_decode_supported(const gva_shape&, bool) { return false; }
+namespace {
 
-DecodePlan plan_mfma_decode(const gva_shape&, int, bool) { return DecodePlan{}; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-hipError_t launch_decode_mfma(const gva_shape&, const DecodePlan&, const DecodeArgs&,
-                              hipStream_t) {
-  return hipErrorInvalidValue;
+constexpr int kTileTok = 16;
+constexpr int kBlock = 64;
+// The running max of a head is raised only when a score exceeds it by this
+// much (log2 units); weights stay below 2^kLazy, far from fp32 limits.
+constexpr float kLazy = 8.0f;
+
+template <int GT, int DH, int DR, bool GQA>
+struct Cfg {
+  static constexpr int KS = DH / 32;                     // 16x16x32 k-steps per group
+  static constexpr int NV = GT * KS;                     // 16-B loads per lane per stream
+  static constexpr int NR = GQA ? 0 : (DR + 15) / 16;    // 16x16x16 k-steps of k_rope
+  static constexpr int NRR = NR > 0 ? NR : 1;
+  static constexpr int DT = DH / 16;                     // 16-dim output tiles
+  static constexpr int ROWB = GT * DH * 2;               // LDS row bytes (one token)
+  static constexpr int WAVE_LDS = 2 * kTileTok * ROWB;   // two tiles per wave
+  static constexpr int REC = DH + 4;                     // record: m, l, pad, pad, acc
+};
+
+// Block-level sizes for NW waves per block.
+template <class C, int NW>
+struct BlockCfg {
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int MERGE = NW * 16 * C::REC * 4;     // wave-merge bytes
+  static constexpr int TILES = NW * C::WAVE_LDS;         // LDS tiles of all waves
+  static constexpr int LDS_BYTES = TILES > MERGE ? TILES : MERGE;
+};
+
+// Row r of a wave's LDS tile keeps its 16-byte chunks XOR-permuted by
+// swz(r): the 16 rows of a tile get distinct permutations, so 16 lanes
+// writing one chunk column hit distinct banks, and 4 consecutive rows read
+// by the transpose load spread over 8 distinct chunks.
+__device__ __forceinline__ int swz(int row) {
+  const int i = row & 15;
+  return ((i << 1) | (i >> 3)) & 15;
+}
+__device__ __forceinline__ int lds_off(int row, int chunk, int ROWB) {
+  return row * ROWB + ((chunk ^ swz(row)) << 4);
+}
+
+__device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Streaming loads of cache rows that are read exactly once (non-temporal).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x4 stream_load16(const bf16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x2 stream_load8(const bf16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+
+// Device-scope (coherent across the chip's L2 slices) stores and loads.
+__device__ __forceinline__ void store_dev2(float* p, float x, float y) {
+  const uint64_t v = static_cast<uint64_t>(__float_as_uint(x)) |
+                     (static_cast<uint64_t>(__float_as_uint(y)) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_dev2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return float2{__uint_as_float(static_cast<uint32_t>(v)),
+                __uint_as_float(static_cast<uint32_t>(v >> 32))};
+}
+
+// Wait until this wave's outstanding global stores are acknowledged
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left unconstrained).
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Compiler-level ordering of a wave's LDS accesses (the hardware keeps a
+// wave's LDS operations in order; lanes of a wave run in lockstep).
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int GT, int DH, int DR, bool GQA>
+struct TileRegs {
+  using C = Cfg<GT, DH, DR, GQA>;
+  u32x4 v[C::NV];                 // value rows (A operand of the score MFMA for GVA)
+  u32x4 k[GQA ? C::NV : 1];       // key rows (GQA only)
+  u32x2 r[C::NRR];                // k_rope rows (GVA only)
+};
+
+// Query operands of one lane (its head = MFMA column), bf16 hi + lo parts.
+template <int GT, int DH, int DR, bool GQA>
+struct QOps {
+  using C = Cfg<GT, DH, DR, GQA>;
+  bf16x8 qh[C::KS], ql[C::KS];    // content slice, k-step s: dims 32s + 8*q4 .. +7
+  s16x4 rh[C::NRR], rl[C::NRR];   // rope slice, k-step s: dims 16s + 4*q4 .. +3
+};
+
+// Running softmax state of one lane's head: max and (this lane's part of
+// the) sum in log2 units, and out^T[16*dt + 4*q4 + r][head] in acc[dt][r].
+template <int GT, int DH, int DR, bool GQA>
+struct SoftState {
+  using C = Cfg<GT, DH, DR, GQA>;
+  float m, l;
+  f32x4 acc[C::DT];
+};
+
+// Per-wave constants.
+struct WaveCtx {
+  const bf16_t* v_base;    // v_pool + group g0 + 8*q4 (row 0)
+  const bf16_t* k_base;    // k_pool (GQA: + group g0 + 8*q4)
+  const int32_t* bt_row;   // block_table row of this sequence
+  size_t vrow;             // elements per value (or key) row
+  int num_blocks, j_begin, j_end, q4, li, lg;
+  unsigned char* lds;      // this wave's LDS tile (2 x 16 rows)
+};
+
+// Loads are issued unconditionally so the compiler can count them in
+// flight (a branch around them makes it wait for every outstanding load).
+// A tile past this wave's last one (k >= n_tiles) reads pool row 0 instead,
+// a valid address whose registers are never used.  A real 16-token tile
+// never leaves its 64-slot block, so slots past the sequence end are still
+// inside the pool; the compute steps keep them out of the result.
+template <int GT, int DH, int DR, bool GQA>
+__device__ __forceinline__ void load_tile(const WaveCtx& w, int k, int n_tiles,
+                                          TileRegs<GT, DH, DR, GQA>& t, int& bad) {
+  using C = Cfg<GT, DH, DR, GQA>;
+  size_t row = 0;
+  if (k < n_tiles) {  // uniform
+    const int j0 = w.j_begin + kTileTok * k;
+    int blk = w.bt_row[j0 / kBlock];
+    if (static_cast<unsigned>(blk) >= static_cast<unsigned>(w.num_blocks)) {
+      bad = 1;
+      blk = 0;  // stay in bounds; the chunk is reported NaN
+    }
+    row = static_cast<size_t>(blk) * kBlock + (j0 % kBlock) + w.li;
+  }
+  const bf16_t* vr = w.v_base + row * w.vrow;
+#pragma unroll
+  for (int g = 0; g < GT; ++g)
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) t.v[g * C::KS + s] = stream_load16(vr + g * DH + 32 * s);
+  if constexpr (GQA) {
+    const bf16_t* kr = w.k_base + row * w.vrow;
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) t.k[g * C::KS + s] = stream_load16(kr + g * DH + 32 * s);
+  } else {
+    const bf16_t* kr = w.k_base + row * DR;
+#pragma unroll
+    for (int s = 0; s < C::NR; ++s) {
+      // lanes past d_r read an in-row address; their query slots are zero
+      const int d = min(16 * s + 4 * w.q4, DR - 4);
+      t.r[s] = stream_load8(kr + d);
+    }
+  }
+}
+
+// Scores of one 16-token tile for this lane's head (tokens 4*q4 .. +3 in
+// log2 units), and the tile's value rows copied into LDS half `half`.
+// Rows past the sequence end carry whatever the slot holds: the caller
+// masks their scores, and their LDS copy is zero.
+template <int GT, int DH, int DR, bool GQA>
+__device__ __forceinline__ f32x4 score_and_stage(const WaveCtx& w, int cnt,
+                                                 const TileRegs<GT, DH, DR, GQA>& t,
+                                                 const QOps<GT, DH, DR, GQA>& qo, int half) {
+  using C = Cfg<GT, DH, DR, GQA>;
+  f32x4 sg[GT];
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      const bf16x8 op =
+          __builtin_bit_cast(bf16x8, GQA ? t.k[g * C::KS + s] : t.v[g * C::KS + s]);
+      a = mfma32(op, qo.qh[s], a);
+      a = mfma32(op, qo.ql[s], a);
+    }
+    sg[g] = a;
+  }
+  f32x4 sc = sg[0];
+#pragma unroll
+  for (int g = 1; g < GT; ++g) sc = (w.lg == g) ? sg[g] : sc;
+  if constexpr (!GQA) {
+    f32x4 sr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < C::NR; ++s) {
+      const s16x4 op = __builtin_bit_cast(s16x4, t.r[s]);
+      sr = mfma16(op, qo.rh[s], sr);
+      sr = mfma16(op, qo.rl[s], sr);
+    }
+    sc += sr;
+  }
+  wave_lds_fence();
+  const int row = 16 * half + w.li;
+  const bool valid = w.li < cnt;
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int g = 0; g < GT; ++g)
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      const int chunk = g * (DH / 8) + 4 * s + w.q4;
+      *reinterpret_cast<u32x4*>(w.lds + lds_off(row, chunk, C::ROWB)) =
+          valid ? t.v[g * C::KS + s] : z4;
+    }
+  return sc;
+}
+
+// Online-softmax update with the 32 scores of a tile pair, then
+// out^T += V_g^T P^T over those 32 tokens.  MFMA k-slot 8*q4 + e of this
+// lane is token 4*q4 + e of the first tile (e < 4) or 4*q4 + e - 4 of the
+// second, in the weights and in the V^T operand alike.
+template <int GT, int DH, int DR, bool GQA>
+__device__ __forceinline__ void softmax_pv(const WaveCtx& w, int cntA, int cntB, f32x4 sa,
+                                           f32x4 sb, SoftState<GT, DH, DR, GQA>& st) {
+  using C = Cfg<GT, DH, DR, GQA>;
+  float sv[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sv[r] = (4 * w.q4 + r < cntA) ? sa[r] : -INFINITY;
+    sv[4 + r] = (4 * w.q4 + r < cntB) ? sb[r] : -INFINITY;
+  }
+  float tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  const bool raise = tmax > st.m + kLazy;
+  if (__any(raise)) {  // uniform: rare after the first pair
+    const float m_new = raise ? tmax : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) st.acc[dt] *= alpha;
+    st.m = m_new;
+  }
+  float p[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sv[j] - st.m);
+  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  bf16x8 ph, pl;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 h = static_cast<__bf16>(p[j]);
+    ph[j] = h;
+    pl[j] = static_cast<__bf16>(p[j] - static_cast<float>(h));
+  }
+  wave_lds_fence();
+  const bf16x8 zero = {};
+  const int r = w.li >> 2, c4 = w.li & 3;
+  const int rowA = 4 * w.q4 + r, rowB = 16 + rowA;
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    const bf16x8 mh = (w.lg == g) ? ph : zero;
+    const bf16x8 ml = (w.lg == g) ? pl : zero;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const int chunk = g * (DH / 8) + 2 * dt + (c4 >> 1);
+      const int within = 8 * (c4 & 1);
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(w.lds + lds_off(rowA, chunk, C::ROWB) + within));
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(w.lds + lds_off(rowB, chunk, C::ROWB) + within));
+      const bf16x8 vt = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+      st.acc[dt] = mfma32(vt, mh, st.acc[dt]);
+      st.acc[dt] = mfma32(vt, ml, st.acc[dt]);
+    }
+  }
+  wave_lds_fence();
+}
+
+// NW: waves per block.  WPE: waves per SIMD the register budget is sized
+// for (2 where the tiles fit in 256 registers without spilling, else 1).
+// NSET: register tile sets in rotation (3, or 2 where three would spill).
+template <int GT, int DH, int DR, bool GQA, int NW, int WPE, int NSET>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void decode_mfma_kernel(
+    const float* __restrict__ q, const bf16_t* __restrict__ v_pool,
+    const bf16_t* __restrict__ k_pool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, int max_seq_len, int H, int G, int max_blocks,
+    int num_blocks, int chunk_tokens, int num_chunks, float q_scale, float* __restrict__ part,
+    unsigned* __restrict__ tickets, float* __restrict__ out, float* __restrict__ lse) {
+  using C = Cfg<GT, DH, DR, GQA>;
+  using BC = BlockCfg<C, NW>;
+  constexpr int kThreads = BC::THREADS;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[BC::LDS_BYTES];
+
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int q4 = lane >> 4, li = lane & 15;
+  const int nht = H / 16;
+  const int ht = wave % nht, sub = wave / nht, nsub = NW / nht;
+
+  int len = seq_lens[b];
+  int bad = (len < 0 || len > max_seq_len || len > max_blocks * kBlock) ? 1 : 0;
+  if (bad) len = 0;
+  const int j_begin = c * chunk_tokens;
+  if (j_begin >= len) {  // uniform over the block
+    if (c == 0) {        // empty or invalid sequence: out = 0 / NaN, lse = -inf / NaN
+      const float v = bad ? __builtin_nanf("") : 0.f;
+      for (int i = threadIdx.x; i < H * DH; i += kThreads)
+        out[static_cast<size_t>(b) * H * DH + i] = v;
+      if (lse)
+        for (int i = threadIdx.x; i < H; i += kThreads)
+          lse[static_cast<size_t>(b) * H + i] = bad ? v : -INFINITY;
+    }
+    return;
+  }
+  const int j_end = min(len, j_begin + chunk_tokens);
+  const int n_tiles = (j_end - j_begin + kTileTok - 1) / kTileTok;
+
+  const int head = ht * 16 + li;     // B-operand column of this lane
+  const int g0 = ht * GT;            // first value group of the head tile
+  constexpr int DQ = GQA ? DH : DH + DR;
+
+  WaveCtx w;
+  w.vrow = static_cast<size_t>(G) * DH;
+  w.v_base = v_pool + static_cast<size_t>(g0) * DH + 8 * q4;
+  w.k_base = GQA ? k_pool + static_cast<size_t>(g0) * DH + 8 * q4 : k_pool;
+  w.bt_row = block_table + static_cast<size_t>(b) * max_blocks;
+  w.num_blocks = num_blocks;
+  w.j_begin = j_begin;
+  w.j_end = j_end;
+  w.q4 = q4;
+  w.li = li;
+  w.lg = li / (16 / GT);
+  w.lds = lds_raw + wave * C::WAVE_LDS;
+
+  // ---- query operands: log2-scaled, split into bf16 hi + lo ----
+  QOps<GT, DH, DR, GQA> qo;
+  {
+    const float qsc = q_scale * kLog2e;
+    const float* qrow = q + (static_cast<size_t>(b) * H + head) * DQ;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      const float4 a = *reinterpret_cast<const float4*>(qrow + 32 * s + 8 * q4);
+      const float4 bb = *reinterpret_cast<const float4*>(qrow + 32 * s + 8 * q4 + 4);
+      const float x[8] = {a.x, a.y, a.z, a.w, bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = qsc * x[e];
+        const __bf16 h = static_cast<__bf16>(v);
+        qo.qh[s][e] = h;
+        qo.ql[s][e] = static_cast<__bf16>(v - static_cast<float>(h));
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < C::NRR; ++s) {
+      bf16x4 hh, ll;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 16 * s + 4 * q4 + e;
+        const float x = (!GQA && d < DR) ? qsc * qrow[DH + d] : 0.f;
+        const __bf16 h = static_cast<__bf16>(x);
+        hh[e] = h;
+        ll[e] = static_cast<__bf16>(x - static_cast<float>(h));
+      }
+      qo.rh[s] = __builtin_bit_cast(s16x4, hh);
+      qo.rl[s] = __builtin_bit_cast(s16x4, ll);
+    }
+  }
+
+  SoftState<GT, DH, DR, GQA> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) st.acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- main loop: this wave's tiles sub + i*nsub, two per step; three
+  // register sets rotate so the next loads go out as soon as a set is free.
+  {
+    auto tile = [&](int i) { return sub + i * nsub; };
+    auto count = [&](int i) {
+      return max(0, min(kTileTok, j_end - (j_begin + kTileTok * tile(i))));
+    };
+    if constexpr (NSET == 3) {
+      TileRegs<GT, DH, DR, GQA> ta, tb, tc;
+      load_tile(w, tile(0), n_tiles, ta, bad);
+      load_tile(w, tile(1), n_tiles, tb, bad);
+      load_tile(w, tile(2), n_tiles, tc, bad);
+      int i = 0;
+      while (tile(i) < n_tiles) {
+        // pair (i, i+1) in (ta, tb)
+        {
+          const f32x4 sa = score_and_stage(w, count(i), ta, qo, 0);
+          load_tile(w, tile(i + 3), n_tiles, ta, bad);
+          const f32x4 sb = score_and_stage(w, count(i + 1), tb, qo, 1);
+          load_tile(w, tile(i + 4), n_tiles, tb, bad);
+          softmax_pv(w, count(i), count(i + 1), sa, sb, st);
+        }
+        i += 2;
+        if (tile(i) >= n_tiles) break;
+        // pair (i, i+1) in (tc, ta)
+        {
+          const f32x4 sa = score_and_stage(w, count(i), tc, qo, 0);
+          load_tile(w, tile(i + 3), n_tiles, tc, bad);
+          const f32x4 sb = score_and_stage(w, count(i + 1), ta, qo, 1);
+          load_tile(w, tile(i + 4), n_tiles, ta, bad);
+          softmax_pv(w, count(i), count(i + 1), sa, sb, st);
+        }
+        i += 2;
+        if (tile(i) >= n_tiles) break;
+        // pair (i, i+1) in (tb, tc)
+        {
+          const f32x4 sa = score_and_stage(w, count(i), tb, qo, 0);
+          load_tile(w, tile(i + 3), n_tiles, tb, bad);
+          const f32x4 sb = score_and_stage(w, count(i + 1), tc, qo, 1);
+          load_tile(w, tile(i + 4), n_tiles, tc, bad);
+          softmax_pv(w, count(i), count(i + 1), sa, sb, st);
+        }
+        i += 2;
+      }
+    } else {
+      TileRegs<GT, DH, DR, GQA> ta, tb;
+      load_tile(w, tile(0), n_tiles, ta, bad);
+      load_tile(w, tile(1), n_tiles, tb, bad);
+      for (int i = 0; tile(i) < n_tiles; i += 2) {
+        const f32x4 sa = score_and_stage(w, count(i), ta, qo, 0);
+        load_tile(w, tile(i + 2), n_tiles, ta, bad);
+        const f32x4 sb = score_and_stage(w, count(i + 1), tb, qo, 1);
+        load_tile(w, tile(i + 3), n_tiles, tb, bad);
+        softmax_pv(w, count(i), count(i + 1), sa, sb, st);
+      }
+    }
+  }
+
+  // ---- merge the waves of each head tile, write one record per head ----
+  float l_run = st.l;
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  bad = __syncthreads_or(bad);
+  float* red = reinterpret_cast<float*>(lds_raw) + wave * 16 * C::REC;
+  if (q4 == 0) {
+    red[li * C::REC] = st.m;
+    red[li * C::REC + 1] = l_run;
+  }
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt)
+    *reinterpret_cast<float4*>(red + li * C::REC + 4 + 16 * dt + 4 * q4) =
+        float4{st.acc[dt][0], st.acc[dt][1], st.acc[dt][2], st.acc[dt][3]};
+  __syncthreads();
+  const float* all = reinterpret_cast<const float*>(lds_raw);
+  float* pb = part + (static_cast<size_t>(b) * num_chunks + c) * H * C::REC;
+  const float nan = __builtin_nanf("");
+  for (int i = threadIdx.x; i < nht * 16 * (DH / 4); i += kThreads) {
+    const int hh = i / (DH / 4);          // head within the block's H
+    const int d4 = (i % (DH / 4)) * 4;
+    const int t_ht = hh / 16, n = hh % 16;
+    float m_star = -INFINITY;
+    for (int wv = t_ht; wv < NW; wv += nht)
+      m_star = fmaxf(m_star, all[(wv * 16 + n) * C::REC]);
+    float L = 0.f;
+    float4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int wv = t_ht; wv < NW; wv += nht) {
+      const float* rr = all + (wv * 16 + n) * C::REC;
+      const float wt = exp2f(rr[0] - m_star);
+      L = fmaf(wt, rr[1], L);
+      const float4 a = *reinterpret_cast<const float4*>(rr + 4 + d4);
+      o.x = fmaf(wt, a.x, o.x);
+      o.y = fmaf(wt, a.y, o.y);
+      o.z = fmaf(wt, a.z, o.z);
+      o.w = fmaf(wt, a.w, o.w);
+    }
+    float* dst = pb + hh * C::REC;
+    store_dev2(dst + 4 + d4, o.x, o.y);
+    store_dev2(dst + 6 + d4, o.z, o.w);
+    if (d4 == 0) store_dev2(dst, m_star, bad ? nan : L);
+  }
+
+  // ---- the last block of this sequence merges its chunk records ----
+  // Records are written and read with device-scope accesses, which go to
+  // the device coherence point instead of a CU-private cache line; the
+  // wait for outstanding stores orders them before the ticket.
+  __shared__ int last_s;
+  const int nc = (len + chunk_tokens - 1) / chunk_tokens;
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last_s = __hip_atomic_fetch_add(tickets + static_cast<size_t>(b) * kTicketStride, 1u,
+                                    __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == static_cast<unsigned>(nc - 1);
+  __syncthreads();
+  if (!last_s) return;
+  // Each thread combines the chunk records of one head for 4 output dims,
+  // U chunks per round: the loads of a round are independent and overlap in
+  // flight, and rounds are combined online (log-sum-exp).
+  const float* sb = part + static_cast<size_t>(b) * num_chunks * H * C::REC;
+  const size_t cstride = static_cast<size_t>(H) * C::REC;
+  for (int i = threadIdx.x; i < H * (DH / 4); i += kThreads) {
+    const int hh = i / (DH / 4);
+    const int d4 = (i % (DH / 4)) * 4;
+    const float* r0 = sb + hh * C::REC;
+    float m_run = -INFINITY, L = 0.f;
+    float4 o = {0.f, 0.f, 0.f, 0.f};
+    constexpr int U = 8;
+    for (int c0 = 0; c0 < nc; c0 += U) {
+      float2 ml[U], a[U], bb[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (c0 + u < nc) {
+          const float* r = r0 + (c0 + u) * cstride;
+          ml[u] = load_dev2(r);
+          a[u] = load_dev2(r + 4 + d4);
+          bb[u] = load_dev2(r + 6 + d4);
+        } else {
+          ml[u] = float2{-INFINITY, 0.f};
+          a[u] = bb[u] = float2{0.f, 0.f};
+        }
+      }
+      float m_new = m_run;
+#pragma unroll
+      for (int u = 0; u < U; ++u) m_new = fmaxf(m_new, ml[u].x);
+      const float sc = exp2f(m_run - m_new);
+      L *= sc;
+      o.x *= sc;
+      o.y *= sc;
+      o.z *= sc;
+      o.w *= sc;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wt = exp2f(ml[u].x - m_new);
+        L = fmaf(wt, ml[u].y, L);
+        o.x = fmaf(wt, a[u].x, o.x);
+        o.y = fmaf(wt, a[u].y, o.y);
+        o.z = fmaf(wt, bb[u].x, o.z);
+        o.w = fmaf(wt, bb[u].y, o.w);
+      }
+      m_run = m_new;
+    }
+    const float inv = 1.f / L;
+    *reinterpret_cast<float4*>(out + (static_cast<size_t>(b) * H + hh) * DH + d4) =
+        float4{o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+    if (lse && d4 == 0) lse[static_cast<size_t>(b) * H + hh] = kLn2 * (m_run + log2f(L));
+  }
+  if (threadIdx.x == 0)  // ready for the next call
+    __hip_atomic_store(tickets + static_cast<size_t>(b) * kTicketStride, 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int GT, int DH, int DR, bool GQA>
+hipError_t launch_one(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
+                      hipStream_t stream) {
+  dim3 grid(plan.num_chunks, s.B);
+  // GVA at d_h = 64: 8 waves per block, 2 per SIMD.  d_h = 128 tiles (and
+  // the two streams of GQA) need the whole register file, 1 wave per SIMD:
+  // 4 waves per block.
+  constexpr int NW = (DH == 64 && !GQA) ? 8 : 4;
+  constexpr int WPE = (DH == 64 && !GQA) ? 2 : 1;
+  constexpr int NSET = (DH == 128 && GQA) ? 2 : 3;
+  if ((s.H / 16) > NW || NW % (s.H / 16) != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_mfma_kernel<GT, DH, DR, GQA, NW, WPE, NSET>), grid, dim3(64 * NW),
+                     0, stream,
+                     a.q, static_cast<const bf16_t*>(a.v_pool),
+                     static_cast<const bf16_t*>(a.k_pool), a.block_table, a.seq_lens,
+                     a.max_seq_len, s.H, s.G, s.max_blocks, s.num_blocks, plan.chunk_tokens,
+                     plan.num_chunks, a.q_scale, a.partials, a.tickets, a.out, a.lse);
+  return hipGetLastError();
+}
+
+typedef hipError_t (*launch_fn)(const gva_shape&, const DecodePlan&, const DecodeArgs&,
+                                hipStream_t);
+
+// Instantiated widths: (groups per head tile, d_h, d_r).
+launch_fn pick(const gva_shape& s, bool gqa) {
+  // head tiles of 16 must divide the waves of a block (4 or 8)
+  if (s.cache_dtype != GVA_BF16 || s.H % 16 != 0) return nullptr;
+  const int nht = s.H / 16;
+  if (nht != 1 && nht != 2 && nht != 4) return nullptr;
+  const int hpg = s.H / s.G;
+  if (hpg != 4) return nullptr;
+  if (gqa) {
+    if (s.d_h == 64) return launch_one<4, 64, 0, true>;
+    if (s.d_h == 128) return launch_one<4, 128, 0, true>;
+    return nullptr;
+  }
+  if (s.d_h == 64 && s.d_r == 16) return launch_one<4, 64, 16, false>;
+  if (s.d_h == 64 && s.d_r == 24) return launch_one<4, 64, 24, false>;
+  if (s.d_h == 64 && s.d_r == 32) return launch_one<4, 64, 32, false>;
+  if (s.d_h == 128 && s.d_r == 16) return launch_one<4, 128, 16, false>;
+  if (s.d_h == 128 && s.d_r == 32) return launch_one<4, 128, 32, false>;
+  return nullptr;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return (v && *v) ? atoi(v) : dflt;
+}
+
+}  // namespace
+
+bool mfma_decode_supported(const gva_shape& s, bool keys_separate) {
+  if (env_int("GVA_FORCE_REF", 0)) return false;
+  return pick(s, keys_separate) != nullptr;
+}
+
+// Chunking: enough blocks to keep every CU streaming (target ~1-2 per CU
+// over B*max_seq_len tokens), chunks a multiple of the cache block.  Depends
+// on the sizes only, so the summation order (and the result bits) is fixed
+// for a given call shape.  GVA_TARGET_BLOCKS overrides the target for tuning.
+DecodePlan plan_mfma_decode(const gva_shape& s, int max_seq_len, bool keys_separate) {
+  (void)keys_separate;
+  DecodePlan p{};
+  p.kernel = kKernelMfma;
+  const int target = env_int("GVA_TARGET_BLOCKS", 256);
+  const long long total = static_cast<long long>(s.B) * (max_seq_len > 0 ? max_seq_len : 1);
+  long long chunk = (total + target - 1) / target;
+  chunk = ((chunk + kBlock - 1) / kBlock) * kBlock;
+  if (chunk < kBlock) chunk = kBlock;
+  p.chunk_tokens = static_cast<int>(chunk);
+  p.num_chunks = max_seq_len > 0 ? static_cast<int>((max_seq_len + chunk - 1) / chunk) : 1;
+  p.partial_floats = static_cast<size_t>(s.B) * p.num_chunks * s.H * (s.d_h + 4);
+  p.ticket_bytes = ticket_bytes(s.B);
+  p.workspace_bytes = p.ticket_bytes + p.partial_floats * sizeof(float);
+  return p;
+}
+
+hipError_t launch_decode_mfma(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
+                              hipStream_t stream) {
+  launch_fn f = pick(s, a.keys_separate);
+  if (!f) return hipErrorInvalidValue;
+  return f(s, plan, a, stream);
 }
 
 }  // namespace gva

@@ -125,60 +125,72 @@ __global__ __launch_bounds__(kThreads) void decode_ref_kernel(
     __syncthreads();
   }
 
-  // partial record per head: [m, l, acc[0..d_h)]
-  const int rec = d_h + 2;
+  // partial record per head: [m, l, 0, 0, acc[0..d_h)]
+  const int rec = d_h + 4;
   float* pb = part + (static_cast<size_t>(b) * num_chunks + c) * H * rec;
   const float nan = __builtin_nanf("");
   for (int h = t; h < H; h += kThreads) {
     pb[h * rec] = m_s[h];
     pb[h * rec + 1] = bad_s ? nan : l_s[h];
+    pb[h * rec + 2] = 0.f;
+    pb[h * rec + 3] = 0.f;
   }
 #pragma unroll
   for (int k = 0; k < kAccMax; ++k) {
     const int o = t + k * kThreads;
     if (o < n_acc) {
       const int h = o / d_h, d = o % d_h;
-      pb[h * rec + 2 + d] = acc[k];
+      pb[h * rec + 4 + d] = acc[k];
     }
   }
 }
 
-// Merge the chunk partials of one sequence:  m* = max m_c, w_c = 2^(m_c-m*),
-// out = sum w_c acc_c / sum w_c l_c,  lse = ln 2 * (m* + log2 sum w_c l_c).
-__global__ __launch_bounds__(kThreads) void merge_kernel(
+// Merge the chunk partials of one (sequence, head), one wave per pair:
+//   m* = max_c m_c,  w_c = 2^(m_c - m*),  L = sum_c w_c l_c,
+//   out = sum_c w_c acc_c / L,  lse = ln 2 * (m* + log2 L).
+// Lanes first take one chunk each for (m, l); then one output dim each.
+constexpr int kMergeMaxChunks = 1024;
+
+__global__ __launch_bounds__(64) void merge_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ seq_lens, int max_seq_len,
     int max_tokens, int H, int d_h, int chunk_tokens, int num_chunks, float* __restrict__ out,
     float* __restrict__ lse) {
-  const int b = blockIdx.x;
-  int len = seq_lens[b];
+  __shared__ float w_s[kMergeMaxChunks];
+  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int len = seq_lens[b];
   const bool bad_len = len < 0 || len > max_seq_len || len > max_tokens;
-  const int rec = d_h + 2;
-  const float* pb = part + static_cast<size_t>(b) * num_chunks * H * rec;
+  const int rec = d_h + 4;
+  float* ob = out + (static_cast<size_t>(b) * H + h) * d_h;
   const float nan = __builtin_nanf("");
   if (bad_len || len == 0) {
-    const float v = bad_len ? nan : 0.f;
-    for (int i = threadIdx.x; i < H * d_h; i += blockDim.x)
-      out[static_cast<size_t>(b) * H * d_h + i] = v;
-    if (lse)
-      for (int h = threadIdx.x; h < H; h += blockDim.x)
-        lse[static_cast<size_t>(b) * H + h] = bad_len ? nan : -INFINITY;
+    for (int d = lane; d < d_h; d += 64) ob[d] = bad_len ? nan : 0.f;
+    if (lse && lane == 0) lse[static_cast<size_t>(b) * H + h] = bad_len ? nan : -INFINITY;
     return;
   }
-  const int nc = (len + chunk_tokens - 1) / chunk_tokens;
-  for (int i = threadIdx.x; i < H * d_h; i += blockDim.x) {
-    const int h = i / d_h, d = i % d_h;
-    float m_star = -INFINITY;
-    for (int c = 0; c < nc; ++c) m_star = fmaxf(m_star, pb[(c * H + h) * rec]);
-    float L = 0.f, o = 0.f;
-    for (int c = 0; c < nc; ++c) {
-      const float* r = pb + (c * H + h) * rec;
-      const float w = exp2f(r[0] - m_star);
-      L = fmaf(w, r[1], L);
-      o = fmaf(w, r[2 + d], o);
-    }
-    out[static_cast<size_t>(b) * H * d_h + i] = o / L;
-    if (lse && d == 0) lse[static_cast<size_t>(b) * H + h] = kLn2 * (m_star + log2f(L));
+  const int nc = min((len + chunk_tokens - 1) / chunk_tokens, num_chunks);
+  const float* pb = part + (static_cast<size_t>(b) * num_chunks * H + h) * rec;
+  const size_t cstride = static_cast<size_t>(H) * rec;  // next chunk, same head
+  float m_star = -INFINITY;
+  for (int c = lane; c < nc; c += 64) m_star = fmaxf(m_star, pb[c * cstride]);
+  m_star = wave_max(m_star);
+  float L = 0.f;
+  for (int c = lane; c < nc; c += 64) {
+    const float w = exp2f(pb[c * cstride] - m_star);
+    L = fmaf(w, pb[c * cstride + 1], L);
+    if (c < kMergeMaxChunks) w_s[c] = w;
   }
+  L = wave_sum(L);
+  __syncthreads();
+  const float inv = 1.f / L;
+  for (int d = lane; d < d_h; d += 64) {
+    float o = 0.f;
+    for (int c = 0; c < nc; ++c) {
+      const float w = c < kMergeMaxChunks ? w_s[c] : exp2f(pb[c * cstride] - m_star);
+      o = fmaf(w, pb[c * cstride + 4 + d], o);
+    }
+    ob[d] = o * inv;
+  }
+  if (lse && lane == 0) lse[static_cast<size_t>(b) * H + h] = kLn2 * (m_star + log2f(L));
 }
 
 }  // namespace
@@ -207,7 +219,12 @@ hipError_t launch_decode_ref(const gva_shape& s, const DecodePlan& plan, const D
 #undef GVA_LAUNCH_REF
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(s.B), dim3(kThreads), 0, stream, a.partials, a.seq_lens,
+  return launch_merge(s, plan, a, stream);
+}
+
+hipError_t launch_merge(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL(merge_kernel, dim3(s.H, s.B), dim3(64), 0, stream, a.partials, a.seq_lens,
                      a.max_seq_len, s.max_blocks * kTile, s.H, s.d_h, plan.chunk_tokens,
                      plan.num_chunks, a.out, a.lse);
   return hipGetLastError();

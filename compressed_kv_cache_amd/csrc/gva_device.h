@@ -50,17 +50,6 @@ template <> struct Cache<bf16_t> {
   static __device__ __forceinline__ bf16_t from_f64(double x) { return f64_to_bf16_rne(x); }
 };
 
-// Rotate the pair (x0, x1) by pos * base^(-2i/d_r), all in float64.
-__device__ __forceinline__ void rope_pair_f64(double x0, double x1, int pos, int i, int d_r,
-                                              double base, double* y0, double* y1) {
-  const double theta = pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(d_r));
-  const double ang = static_cast<double>(pos) * theta;
-  double s, c;
-  sincos(ang, &s, &c);
-  *y0 = x0 * c - x1 * s;
-  *y1 = x0 * s + x1 * c;
-}
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -16,8 +16,16 @@ struct DecodePlan {
   int chunk_tokens;  // tokens per split chunk (multiple of the block size)
   int num_chunks;    // chunks per sequence = ceil(max_seq_len / chunk_tokens)
   size_t partial_floats;  // floats of split partial results
+  size_t ticket_bytes;    // per-sequence completion counters at the workspace start
   size_t workspace_bytes;
 };
+
+// Workspace = [B counters, one per 256 B][partial records].  A counter per
+// 256 B keeps the blocks of different sequences from contending for one
+// memory channel.  The counters must be zero before the first call; every
+// call leaves them zero.
+constexpr int kTicketStride = 64;  // u32 elements between counters
+inline size_t ticket_bytes(int B) { return static_cast<size_t>(B) * kTicketStride * 4; }
 
 enum { kKernelRef = 0, kKernelMfma = 1 };
 
@@ -32,6 +40,14 @@ hipError_t launch_append(const gva_shape& s, const float* v_new, const float* k_
                          const int32_t* pos, const int32_t* block_table, double base,
                          void* v_pool, void* k_pool, hipStream_t stream);
 
+// Absorption (q_nope != nullptr) and append (v_new != nullptr) in one launch;
+// the position of sequence b is pos[b] + pos_offset.
+hipError_t launch_prologue(const gva_shape& s, const float* q_nope, const float* q_rope,
+                           const float* M, float scale, float* qa, const float* v_new,
+                           const float* k_new, const int32_t* block_table, void* v_pool,
+                           void* k_pool, const int32_t* pos, int pos_offset, double base,
+                           hipStream_t stream);
+
 // GVA decode (keys_separate = false: the key of head h is [V_g(h) | k_rope],
 // query already scaled) and GQA decode (keys_separate = true: key K_g(h),
 // query scaled by `scale` inside the kernel) share one launcher.
@@ -43,13 +59,17 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   int max_seq_len;
   float* partials;
+  unsigned* tickets;
   float* out;
   float* lse;
   float q_scale;          // multiplies q inside the kernel
   bool keys_separate;
 };
 
-hipError_t launch_decode(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
-                         hipStream_t stream);
+// Log-sum-exp merge of the per-chunk partial records
+// part[B][num_chunks][H][d_h + 4] = (max, sum, 0, 0, unnormalised accumulator) into
+// out[B][H][d_h] and lse[B][H] (scores in log2 units).
+hipError_t launch_merge(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
+                        hipStream_t stream);
 
 }  // namespace gva

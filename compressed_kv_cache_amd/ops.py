@@ -113,7 +113,8 @@ def _decode_shape(B, H, v_pool, d_r, block_table, keys_separate=False):
 
 
 def decode_workspace_bytes(B, H, v_pool, k_pool, block_table, max_seq_len):
-    """Workspace size gva_decode_attention needs for these caches."""
+    """Workspace size gva_decode_attention needs for these caches.  A
+    workspace must be zero-filled once when allocated (torch.zeros)."""
     s = _decode_shape(B, H, v_pool, k_pool.shape[2], block_table)
     n = ctypes.c_size_t(0)
     check("gva_decode_workspace_size", _lib.load().gva_decode_workspace_size(
@@ -121,9 +122,20 @@ def decode_workspace_bytes(B, H, v_pool, k_pool, block_table, max_seq_len):
     return n.value
 
 
+def gqa_decode_workspace_bytes(B, H, k_pool, v_pool, block_table, max_seq_len):
+    """Workspace size gqa_decode_attention needs for these caches."""
+    s = _decode_shape(B, H, v_pool, 0, block_table, True)
+    n = ctypes.c_size_t(0)
+    check("gqa_decode_workspace_size", _lib.load().gqa_decode_workspace_size(
+        ctypes.byref(s), int(max_seq_len), ctypes.byref(n)))
+    return n.value
+
+
 def _workspace(nbytes, dev, workspace):
+    # zero-filled on allocation: the per-sequence counters at its start must
+    # be zero before the first call (each call leaves them zero again)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
     if workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError("workspace too small")
     return workspace
@@ -192,4 +204,63 @@ def gqa_decode_attention(q, k_pool, v_pool, block_table, seq_lens, max_seq_len,
         _ptr(workspace), workspace.numel() * workspace.element_size(),
         _ptr(out), _ptr(lse), _stream(dev))
     check("gqa_decode_attention", st)
+    return out, lse
+
+
+def decode_step_workspace_bytes(q_nope, q_rope, v_pool, k_pool, block_table, max_seq_len):
+    """Workspace size gva_decode_step needs (zero-fill it once when allocated)."""
+    B, H, d_n = q_nope.shape
+    NB, bs, G, d_h = v_pool.shape
+    s = GvaShape(B, H, G, d_h, d_n, q_rope.shape[2], bs, block_table.shape[1], NB,
+                 _cache_dtype(v_pool, "v_pool"))
+    n = ctypes.c_size_t(0)
+    check("gva_decode_step_workspace_size", _lib.load().gva_decode_step_workspace_size(
+        ctypes.byref(s), int(max_seq_len), ctypes.byref(n)))
+    return n.value
+
+
+def decode_step(q_nope, q_rope, M, v_pool, k_pool, block_table, seq_lens, max_seq_len,
+                v_new=None, k_new=None, softmax_scale=None, rope_base=10000.0,
+                workspace=None, out=None, lse=None, want_lse=True):
+    """Append (if v_new/k_new are given) + absorb + decode in two launches
+    (gva_decode_step).  The new token and the query sit at seq_lens - 1."""
+    dev = v_pool.device
+    _need(q_nope, "q_nope", torch.float32, dev, 3)
+    _need(q_rope, "q_rope", torch.float32, dev, 3)
+    _need(M, "M", torch.float32, dev, 3)
+    _need(v_pool, "v_pool", v_pool.dtype, dev, 4)
+    _need(k_pool, "k_pool", v_pool.dtype, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    B, H, d_n = q_nope.shape
+    NB, bs, G, d_h = v_pool.shape
+    d_r = q_rope.shape[2]
+    if tuple(q_rope.shape[:2]) != (B, H) or tuple(M.shape) != (H, d_h, d_n) \
+            or tuple(k_pool.shape) != (NB, bs, d_r) or block_table.shape[0] != B \
+            or seq_lens.shape[0] != B:
+        raise ValueError("inconsistent shapes for decode_step")
+    if (v_new is None) != (k_new is None):
+        raise ValueError("give both v_new and k_new, or neither")
+    if v_new is not None:
+        _need(v_new, "v_new", torch.float32, dev, 3)
+        _need(k_new, "k_new", torch.float32, dev, 2)
+        if tuple(v_new.shape) != (B, G, d_h) or tuple(k_new.shape) != (B, d_r):
+            raise ValueError("inconsistent shapes for v_new / k_new")
+    s = GvaShape(B, H, G, d_h, d_n, d_r, bs, block_table.shape[1], NB,
+                 _cache_dtype(v_pool, "v_pool"))
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    check("gva_decode_step_workspace_size", lib.gva_decode_step_workspace_size(
+        ctypes.byref(s), int(max_seq_len), ctypes.byref(n)))
+    workspace = _workspace(n.value, dev, workspace)
+    if out is None:
+        out = torch.empty((B, H, d_h), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    st = lib.gva_decode_step(
+        ctypes.byref(s), _ptr(q_nope), _ptr(q_rope), _ptr(M), float(softmax_scale or 0.0),
+        float(rope_base), _ptr(v_new), _ptr(k_new), _ptr(v_pool), _ptr(k_pool),
+        _ptr(block_table), _ptr(seq_lens), int(max_seq_len), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(dev))
+    check("gva_decode_step", st)
     return out, lse

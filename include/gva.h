@@ -134,7 +134,11 @@ gva_status gva_append_cache(const gva_shape* shape, const float* v_new,
                             void* v_pool, void* k_pool, void* stream);
 
 /* Bytes of workspace gva_decode_attention needs for these sizes and this
- * upper bound on sequence length (split-context partial results). */
+ * upper bound on sequence length: per-sequence completion counters followed
+ * by the split-context partial results.  A workspace must be zero-filled
+ * once, when it is allocated; every call leaves its counters zero again, so
+ * it can be reused (and captured in graphs) without clearing.  Calls that
+ * run concurrently need separate workspaces. */
 gva_status gva_decode_workspace_size(const gva_shape* shape,
                                      int32_t max_seq_len, size_t* bytes);
 
@@ -153,8 +157,9 @@ gva_status gva_decode_workspace_size(const gva_shape* shape,
  *   qa [B][H][d_h + d_r] f32 (16B), v_pool/k_pool (16B), block_table
  *   [B][max_blocks] i32, seq_lens [B] i32 on the device, each
  *   <= min(max_seq_len, max_blocks*block_size); max_seq_len (host) >= 0;
- *   workspace of at least gva_decode_workspace_size bytes (16B; contents
- *   undefined afterwards); out [B][H][d_h] f32 (16B); lse [B][H] f32 or NULL.
+ *   workspace of at least gva_decode_workspace_size bytes (16B, zero-filled
+ *   at allocation, see above); out [B][H][d_h] f32 (16B); lse [B][H] f32 or
+ *   NULL.
  * seq_lens[b] == 0 gives out = 0 and lse = -inf.  Uses every shape field
  * except d_n. */
 gva_status gva_decode_attention(const gva_shape* shape, const float* qa,
@@ -163,6 +168,29 @@ gva_status gva_decode_attention(const gva_shape* shape, const float* qa,
                                 const int32_t* seq_lens, int32_t max_seq_len,
                                 void* workspace, size_t workspace_bytes,
                                 float* out, float* lse, void* stream);
+
+/* One decode step in two launches: append each sequence's new token (when
+ * v_new and k_new are given; both or neither), absorb the maps into the
+ * queries, and run gva_decode_attention -- the calls above, fused.  The new
+ * token and the query sit at position seq_lens[b] - 1 (seq_lens already
+ * counts the new token).  The absorbed query lives in the workspace.
+ *   q_nope, q_rope, M, softmax_scale, rope_base as gva_absorb_query;
+ *   v_new, k_new as gva_append_cache, or both NULL; v_pool, k_pool,
+ *   block_table, seq_lens, max_seq_len, out, lse as gva_decode_attention;
+ *   workspace of at least gva_decode_step_workspace_size bytes (16B,
+ *   zero-filled at allocation like the decode workspace).
+ * Uses every shape field. */
+gva_status gva_decode_step_workspace_size(const gva_shape* shape,
+                                          int32_t max_seq_len, size_t* bytes);
+gva_status gva_decode_step(const gva_shape* shape, const float* q_nope,
+                           const float* q_rope, const float* M,
+                           float softmax_scale, float rope_base,
+                           const float* v_new, const float* k_new,
+                           void* v_pool, void* k_pool,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           int32_t max_seq_len, void* workspace,
+                           size_t workspace_bytes, float* out, float* lse,
+                           void* stream);
 
 /* Same-shape grouped-query attention decode, the baseline GVA is compared
  * with: each group stores both a key and a value row per token

@@ -308,3 +308,89 @@ def test_gqa_small_fp32(g, gpu):
     ref, ref_lse = o.gqa_decode(h["q"], h["k_pool"], h["v_pool"], h["block_table"],
                                 h["seq_lens"])
     assert_fp32_parity(cpu(out), ref)
+
+
+def test_reference_kernel_on_matrix_core_shapes(g, gpu, monkeypatch):
+    """The plain VALU kernel, forced on a bf16 shape the matrix-core kernel
+    normally takes, agrees with the oracle and (to rounding) with it."""
+    cfg = syn.with_overrides(syn.get_config("decode_350m"), B=3, T=None,
+                             len_range=(1, 2000), shuffled_blocks=True)
+    x, h = gen(cfg, gpu)
+    qa = g.absorb_query(x["q_nope"], x["q_rope"], x["M"], x["pos"])
+    fast, _ = g.decode_attention(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                 x["seq_lens"], x["max_seq_len"])
+    monkeypatch.setenv("GVA_FORCE_REF", "1")
+    ref_k, _ = g.decode_attention(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                  x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    ref, _ = o.gva_decode_materialized(h["q_nope"], h["q_rope"], h["M"], h["v_pool"],
+                                       h["k_pool"], h["block_table"], h["seq_lens"])
+    assert_bf16_parity(cpu(ref_k).double().numpy(), ref, what="reference kernel")
+    assert_bf16_parity(cpu(fast).double().numpy(), ref, what="matrix-core kernel")
+
+
+def test_workspace_reused_across_calls(g, gpu):
+    """One zero-filled workspace serves many calls with different lengths (the
+    per-sequence counters reset themselves): every call matches a call with
+    a fresh workspace bit for bit."""
+    cfg = syn.with_overrides(syn.get_config("long_ragged"), len_range=(3000, 20000))
+    x, _ = gen(cfg, gpu)
+    qa = g.absorb_query(x["q_nope"], x["q_rope"], x["M"], x["pos"])
+    mx = x["max_seq_len"]
+    ws = torch.zeros(g.decode_workspace_bytes(cfg.B, cfg.H, x["v_pool"], x["k_pool"],
+                                              x["block_table"], mx),
+                     dtype=torch.uint8, device=gpu)
+    full = x["seq_lens"]
+    variants = [full, (full // 3).clamp_min(1), full.clamp_max(64), full,
+                torch.zeros_like(full), full]
+    for i, lens in enumerate(variants):
+        a, la = g.decode_attention(qa, x["v_pool"], x["k_pool"], x["block_table"], lens, mx,
+                                   workspace=ws)
+        b, lb = g.decode_attention(qa, x["v_pool"], x["k_pool"], x["block_table"], lens, mx)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b) and torch.equal(la, lb), f"call {i}"
+
+
+# ------------------------------------------------------------ fused step ----
+
+@pytest.mark.parametrize("name,kw", [
+    ("wide_rope_append", {"B": 8, "T": 3000}),
+    ("decode_350m", {"B": 4, "T": 1000, "append": True}),
+    ("tiny_fp32", {"append": True}),
+    ("large_model", {"B": 4, "T": 700, "append": True}),
+])
+def test_decode_step_matches_oracle_and_separate_calls(g, gpu, name, kw):
+    """gva_decode_step (append + absorb + decode in two launches) equals the
+    oracle, and equals the three separate calls bit for bit."""
+    cfg = syn.with_overrides(syn.get_config(name), **kw)
+    announce("decode_step", name, kw)
+    x, h = gen(cfg, gpu)
+    vp0, kp0 = x["v_pool"].clone(), x["k_pool"].clone()
+    out, lse = g.decode_step(x["q_nope"], x["q_rope"], x["M"], x["v_pool"], x["k_pool"],
+                             x["block_table"], x["seq_lens"], x["max_seq_len"],
+                             v_new=x["v_new"], k_new=x["k_new"], rope_base=cfg.rope_base)
+    torch.cuda.synchronize()
+    # the same through the separate entry points, on fresh copies of the caches
+    x2 = dict(x)
+    x2["v_pool"], x2["k_pool"] = vp0, kp0
+    _, out2, lse2 = run_step(g, x2, cfg)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    assert torch.equal(x["v_pool"].nan_to_num(7), vp0.nan_to_num(7))
+    assert torch.equal(x["k_pool"].nan_to_num(7), kp0.nan_to_num(7))
+    vp, kp = oracle_pools(h, cfg)
+    ref, ref_lse = o.gva_decode_materialized(
+        h["q_nope"], h["q_rope"], h["M"], vp, kp, h["block_table"], h["seq_lens"],
+        base=cfg.rope_base)
+    if cfg.cache_dtype == "float32":
+        assert_fp32_parity(cpu(out), ref)
+    else:
+        assert_bf16_parity(cpu(out).double().numpy(), ref)
+
+
+def test_decode_step_without_append(g, gpu):
+    cfg = syn.with_overrides(syn.get_config("long_ragged"), len_range=(100, 3000))
+    x, h = gen(cfg, gpu)
+    out, _ = g.decode_step(x["q_nope"], x["q_rope"], x["M"], x["v_pool"], x["k_pool"],
+                           x["block_table"], x["seq_lens"], x["max_seq_len"])
+    _, out2, _ = run_step(g, x, cfg)
+    assert torch.equal(out, out2)
