@@ -1,8 +1,9 @@
 // Per-token prologue of a GVA decode step: query absorption and the cache
 // append, in one launch.  Both touch O(B*H*d_h*d_n) and O(B*G*d_h) data,
-// negligible next to the cache scan, so the kernel is built for latency: one
-// thread per output, every load issued up front, and the RoPE frequencies
-// taken from a float64 table computed on the host.
+// negligible next to the cache scan, so the kernel is built for latency:
+// one-wave blocks spread over the chip, every global load a lane needs
+// issued before the first wait, and the RoPE frequencies taken from a
+// float64 table computed on the host.
 #include <math.h>
 
 #include "gva_device.h"
@@ -12,8 +13,11 @@ namespace gva {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 64;     // one wave per block: many small blocks spread the latency
 constexpr int kMaxHalfRope = 32;  // d_r <= 64
+constexpr int kKBatch = 16;       // k-steps whose operands are loaded before one wait
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // theta_i = base^(-2i/d_r), i < d_r/2, in float64.
 struct RopeTable {
@@ -36,6 +40,7 @@ struct PrologueArgs {
   const int32_t* pos;  // position of sequence b: pos[b] + pos_offset
   int pos_offset;
   int B, H, G, d_h, d_n, d_r, bs, max_blocks, num_blocks;
+  int absorb_blocks;   // blocks [0, absorb_blocks) absorb, the rest append
 };
 
 // Rotate (x0, x1) by angle pos * theta (float64).
@@ -47,76 +52,138 @@ __device__ __forceinline__ void rotate_f64(double x0, double x1, int pos, double
   *y1 = x0 * s + x1 * c;
 }
 
-// Block (hx, by) covers sequences by*BT .. by*BT+BT-1, BT = 256/d_h.
-//  absorb:  head hx; thread (bl, e) writes
-//           qa[b][h][e] = s * sum_n q_nope[b][h][n] M[h][e][n]      (e < d_h)
-//           and the first BT*d_r/2 threads the rotated position slice
-//           qa[b][h][d_h + 2i, 2i+1] = s * R(pos_b) q_rope[b][h]
-//           (the fixed map M_h folds into the query once per token:
-//           onedev.kr review, "How it works"; bisque.today, Equation 7);
-//  append:  blocks with hx == 0 write each sequence's new token: values
-//           rounded once into the cache dtype, and the positional key
-//           rotated to its position in float64 and rounded once (the key is
-//           cached already rotated: onedev.kr review, "How it differs").
+// Absorption, one 16 x 16 output tile per wave: sequences b0 .. b0+15 and
+// content dims e0 .. e0+15 of head h,
+//   qa[b][h][e] = s * sum_n q_nope[b][h][n] M[h][e][n],
+// a (16 x d_n) x (d_n x 16) product on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32: lane l feeds A[l%16][l/16] and B[l/16][l%16] and
+// holds D[4(l/16)+r][l%16]).  Lane group l/16 sums the contiguous n range
+// [kg*K4, kg*K4 + K4), K4 = ceil(d_n/4), so each lane's loads are
+// contiguous.  The waves of (h, b0) also write the rotated position slice
+// qa[b][h][d_h + 2i, 2i+1] = s * R(pos_b) q_rope[b][h] (float64 rotation).
+// The fixed map M_h folds into the query once per token (onedev.kr review,
+// "How it works"; bisque.today, Equation 7).
+__device__ __forceinline__ void absorb_block(const PrologueArgs& a, const RopeTable& rt,
+                                             int id) {
+  const int lane = threadIdx.x;
+  const int DT = a.d_h / 16;
+  const int et = id % DT, rest = id / DT;
+  const int h = rest % a.H, b0 = (rest / a.H) * 16;
+  const int li = lane & 15, kg = lane >> 4;
+  const int half = a.d_r / 2;
+  const int dq = a.d_h + a.d_r;
+
+  // position-slice inputs of this lane's first pair, loaded with the rest
+  const int npairs = 16 * half;
+  int pi = et * 64 + lane;
+  int p_seq = min(pi / half, 15), p_i = pi % half;
+  int p_b = min(b0 + p_seq, a.B - 1);
+  const float* xr = a.q_rope + (static_cast<size_t>(p_b) * a.H + h) * a.d_r + 2 * p_i;
+  float x0 = xr[0], x1 = xr[1];
+  int p_pos = a.pos[p_b] + a.pos_offset;
+
+  const int K4 = (a.d_n + 3) / 4;
+  const int bq = min(b0 + li, a.B - 1);
+  const float* qrow = a.q_nope + (static_cast<size_t>(bq) * a.H + h) * a.d_n;
+  const float* mrow = a.M + (static_cast<size_t>(h) * a.d_h + et * 16 + li) * a.d_n;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < K4; s0 += kKBatch) {
+    float qv[kKBatch], mv[kKBatch];
+#pragma unroll
+    for (int s = 0; s < kKBatch; ++s) {
+      const int n = kg * K4 + s0 + s;
+      const int nc = min(n, a.d_n - 1);
+      qv[s] = qrow[nc];
+      mv[s] = mrow[nc];
+    }
+#pragma unroll
+    for (int s = 0; s < kKBatch; ++s) {
+      const bool ok = (s0 + s < K4) && (kg * K4 + s0 + s < a.d_n);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ok ? qv[s] : 0.f, ok ? mv[s] : 0.f, acc, 0, 0,
+                                                 0);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int b = b0 + 4 * kg + r;
+    if (b < a.B) a.qa[(static_cast<size_t>(b) * a.H + h) * dq + et * 16 + li] = a.scale * acc[r];
+  }
+
+  const double sc = static_cast<double>(a.scale);
+  for (;;) {
+    if (pi < npairs && b0 + p_seq < a.B) {
+      double y0, y1;
+      rotate_f64(x0, x1, p_pos, rt.theta[p_i], &y0, &y1);
+      float* dst = a.qa + (static_cast<size_t>(p_b) * a.H + h) * dq + a.d_h + 2 * p_i;
+      dst[0] = static_cast<float>(sc * y0);
+      dst[1] = static_cast<float>(sc * y1);
+    }
+    pi += DT * 64;
+    if (pi >= npairs) break;
+    p_seq = pi / half;
+    p_i = pi % half;
+    p_b = min(b0 + p_seq, a.B - 1);
+    xr = a.q_rope + (static_cast<size_t>(p_b) * a.H + h) * a.d_r + 2 * p_i;
+    x0 = xr[0];
+    x1 = xr[1];
+    p_pos = a.pos[p_b] + a.pos_offset;
+  }
+}
+
+__device__ __forceinline__ void store4(float* p, float x0, float x1, float x2, float x3) {
+  *reinterpret_cast<float4*>(p) = make_float4(x0, x1, x2, x3);
+}
+__device__ __forceinline__ void store4(bf16_t* p, float x0, float x1, float x2, float x3) {
+  uint2 w;
+  w.x = static_cast<uint32_t>(f32_to_bf16_rne(x0)) |
+        (static_cast<uint32_t>(f32_to_bf16_rne(x1)) << 16);
+  w.y = static_cast<uint32_t>(f32_to_bf16_rne(x2)) |
+        (static_cast<uint32_t>(f32_to_bf16_rne(x3)) << 16);
+  *reinterpret_cast<uint2*>(p) = w;
+}
+
+// Append: one thread per four values or per rotary pair of one sequence's
+// new token.  Values are rounded once into the cache dtype; the positional
+// key is rotated to its position in float64 and rounded once (the key is
+// cached already rotated: onedev.kr review, "How it differs").  A position
+// or block-table entry out of range skips the write.
+template <typename CT>
+__device__ __forceinline__ void append_block(const PrologueArgs& a, const RopeTable& rt,
+                                             int id) {
+  const int nv = a.G * a.d_h, nq = nv / 4, half = a.d_r / 2, per_b = nq + half;
+  const int idx = id * kThreads + static_cast<int>(threadIdx.x);
+  if (idx >= a.B * per_b) return;
+  const int b = idx / per_b, r = idx - b * per_b;
+  const bool is_v = r < nq;
+  const int i = r - nq;
+  // all loads first: the position, then the four (or two) source scalars
+  const int p = a.pos[b] + a.pos_offset;
+  const float* s0 = is_v ? a.v_new + static_cast<size_t>(b) * nv + 4 * r
+                         : a.k_new + static_cast<size_t>(b) * a.d_r + 2 * i;
+  const float* s1 = is_v ? s0 + 2 : s0;
+  const float x0 = s0[0], x1 = s0[1], x2 = s1[0], x3 = s1[1];
+  if (p < 0 || p >= a.max_blocks * a.bs) return;
+  const int blk = a.block_table[static_cast<size_t>(b) * a.max_blocks + p / a.bs];
+  if (blk < 0 || blk >= a.num_blocks) return;
+  const size_t row = static_cast<size_t>(blk) * a.bs + (p % a.bs);
+  if (is_v) {
+    store4(static_cast<CT*>(a.v_pool) + row * nv + 4 * r, x0, x1, x2, x3);
+  } else {
+    double y0, y1;
+    rotate_f64(x0, x1, p, rt.theta[i], &y0, &y1);
+    CT* k = static_cast<CT*>(a.k_pool) + row * a.d_r + 2 * i;
+    k[0] = Cache<CT>::from_f64(y0);
+    k[1] = Cache<CT>::from_f64(y1);
+  }
+}
+
 template <typename CT>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a, RopeTable rt) {
-  const int t = threadIdx.x;
-  const int BT = kThreads / a.d_h;
-  const int b0 = blockIdx.y * BT;
-  const int half = a.d_r / 2;
-
-  if (a.q_nope) {
-    const int h = blockIdx.x;
-    const int dq = a.d_h + a.d_r;
-    {
-      const int bl = t / a.d_h, e = t % a.d_h, b = b0 + bl;
-      if (b < a.B) {
-        const float* qr = a.q_nope + (static_cast<size_t>(b) * a.H + h) * a.d_n;
-        const float* mr = a.M + (static_cast<size_t>(h) * a.d_h + e) * a.d_n;
-        float acc = 0.f;
-#pragma unroll 8
-        for (int n = 0; n < a.d_n; ++n) acc = fmaf(qr[n], mr[n], acc);
-        a.qa[(static_cast<size_t>(b) * a.H + h) * dq + e] = a.scale * acc;
-      }
-    }
-    if (t < BT * half) {
-      const int bl = t / half, i = t % half, b = b0 + bl;
-      if (b < a.B) {
-        const float* x = a.q_rope + (static_cast<size_t>(b) * a.H + h) * a.d_r;
-        double y0, y1;
-        rotate_f64(x[2 * i], x[2 * i + 1], a.pos[b] + a.pos_offset, rt.theta[i], &y0, &y1);
-        float* dst = a.qa + (static_cast<size_t>(b) * a.H + h) * dq + a.d_h;
-        const double s = static_cast<double>(a.scale);
-        dst[2 * i] = static_cast<float>(s * y0);
-        dst[2 * i + 1] = static_cast<float>(s * y1);
-      }
-    }
-  }
-
-  if (a.v_new && blockIdx.x == 0) {
-    CT* v_pool = static_cast<CT*>(a.v_pool);
-    CT* k_pool = static_cast<CT*>(a.k_pool);
-    const int nv = a.G * a.d_h;
-    for (int idx = t; idx < BT * (nv + half); idx += kThreads) {
-      const int bl = idx / (nv + half), r = idx % (nv + half), b = b0 + bl;
-      if (b >= a.B) continue;
-      const int p = a.pos[b] + a.pos_offset;
-      if (p < 0 || p >= a.max_blocks * a.bs) continue;  // out of range: skipped
-      const int blk = a.block_table[static_cast<size_t>(b) * a.max_blocks + p / a.bs];
-      if (blk < 0 || blk >= a.num_blocks) continue;
-      const size_t row = static_cast<size_t>(blk) * a.bs + (p % a.bs);
-      if (r < nv) {
-        v_pool[row * nv + r] = Cache<CT>::from_f32(a.v_new[static_cast<size_t>(b) * nv + r]);
-      } else {
-        const int i = r - nv;
-        const float* x = a.k_new + static_cast<size_t>(b) * a.d_r;
-        double y0, y1;
-        rotate_f64(x[2 * i], x[2 * i + 1], p, rt.theta[i], &y0, &y1);
-        k_pool[row * a.d_r + 2 * i] = Cache<CT>::from_f64(y0);
-        k_pool[row * a.d_r + 2 * i + 1] = Cache<CT>::from_f64(y1);
-      }
-    }
-  }
+  const int id = blockIdx.x;
+  if (id < a.absorb_blocks)
+    absorb_block(a, rt, id);
+  else
+    append_block<CT>(a, rt, id - a.absorb_blocks);
 }
 
 RopeTable rope_table(int d_r, double base) {
@@ -126,17 +193,6 @@ RopeTable rope_table(int d_r, double base) {
   return rt;
 }
 
-hipError_t launch(const PrologueArgs& a, int cache_dtype, double base, hipStream_t stream) {
-  const int BT = kThreads / a.d_h;
-  dim3 grid(a.q_nope ? a.H : 1, (a.B + BT - 1) / BT);
-  const RopeTable rt = rope_table(a.d_r, base);
-  if (cache_dtype == GVA_BF16)
-    hipLaunchKernelGGL(prologue_kernel<bf16_t>, grid, dim3(kThreads), 0, stream, a, rt);
-  else
-    hipLaunchKernelGGL(prologue_kernel<float>, grid, dim3(kThreads), 0, stream, a, rt);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_prologue(const gva_shape& s, const float* q_nope, const float* q_rope,
@@ -144,6 +200,7 @@ hipError_t launch_prologue(const gva_shape& s, const float* q_nope, const float*
                            const float* k_new, const int32_t* block_table, void* v_pool,
                            void* k_pool, const int32_t* pos, int pos_offset, double base,
                            hipStream_t stream) {
+  if (s.d_h % 16 || s.d_r / 2 > kMaxHalfRope || s.d_r < 2) return hipErrorInvalidValue;
   PrologueArgs a{};
   a.pos_offset = pos_offset;
   a.q_nope = q_nope;
@@ -166,7 +223,17 @@ hipError_t launch_prologue(const gva_shape& s, const float* q_nope, const float*
   a.bs = s.block_size;
   a.max_blocks = s.max_blocks;
   a.num_blocks = s.num_blocks;
-  return launch(a, s.cache_dtype, base, stream);
+  a.absorb_blocks = q_nope ? s.H * ((s.B + 15) / 16) * (s.d_h / 16) : 0;
+  const long long append_items =
+      v_new ? static_cast<long long>(s.B) * (s.G * s.d_h / 4 + s.d_r / 2) : 0;
+  const int blocks = a.absorb_blocks + static_cast<int>((append_items + kThreads - 1) / kThreads);
+  if (blocks == 0) return hipSuccess;
+  const RopeTable rt = rope_table(s.d_r, base);
+  if (s.cache_dtype == GVA_BF16)
+    hipLaunchKernelGGL(prologue_kernel<bf16_t>, dim3(blocks), dim3(kThreads), 0, stream, a, rt);
+  else
+    hipLaunchKernelGGL(prologue_kernel<float>, dim3(blocks), dim3(kThreads), 0, stream, a, rt);
+  return hipGetLastError();
 }
 
 hipError_t launch_absorb(const gva_shape& s, const float* q_nope, const float* q_rope,
