@@ -13,9 +13,16 @@ steps; `roofline` covers the decode kernel alone (HIP events around each of
 its launches); `cpu_baseline` is the float64 oracle timed on host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-       python bench.py --copy-calibration     (plain copy for counter scaling)
+       python bench.py --decode-only --steps K   (decode launches alone, for
+                                                  rocprofv3 --pmc runs)
+       python bench.py --copy-calibration        (plain copy for counter scaling)
+       python bench.py --ingest-counters FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+           (reads the four rocprofv3 --pmc output folders, writes
+            profiles/traffic.json and profiles/<workload>_decode_traffic.txt)
 """
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import math
@@ -53,14 +60,19 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gqa", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--decode-only", action="store_true")
+    ap.add_argument("--ingest-counters", nargs=4, metavar="DIR")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time for the oracle sample")
     return ap.parse_args()
 
 
+COPY_BYTES = 256 << 20
+
+
 def copy_calibration(torch, steps):
     """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
-    n = 256 << 20
+    n = COPY_BYTES
     src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(steps):
@@ -70,12 +82,80 @@ def copy_calibration(torch, steps):
                       "launches": steps}))
 
 
+def counter_per_dispatch(folder, counter):
+    """{kernel name: (average counter value per dispatch, dispatches)} from a
+    rocprofv3 --pmc output folder (rows of one dispatch are summed)."""
+    sums, disp = {}, {}
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = r["Kernel_Name"]
+                sums[k] = sums.get(k, 0.0) + float(r["Counter_Value"])
+                disp.setdefault(k, set()).add(r["Dispatch_Id"])
+    return {k: (sums[k] / len(disp[k]), len(disp[k])) for k in sums}
+
+
+def pick_kernel(table, needle):
+    hits = [(k, v) for k, v in table.items() if needle in k]
+    if not hits:
+        raise SystemExit(f"no kernel matching {needle!r} in counter output")
+    return max(hits, key=lambda kv: kv[1][1])
+
+
+def ingest_counters(dirs, workload):
+    """HBM traffic of the decode kernel from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for a plain copy of
+    known size."""
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
+    n_copy = COPY_BYTES
+    _, (c_fetch, _) = pick_kernel(counter_per_dispatch(cfetch_dir, "FETCH_SIZE"), "copyBuffer")
+    _, (c_write, _) = pick_kernel(counter_per_dispatch(cwrite_dir, "WRITE_SIZE"), "copyBuffer")
+    name, (d_fetch, nd) = pick_kernel(counter_per_dispatch(fetch_dir, "FETCH_SIZE"),
+                                      "decode_mfma_kernel")
+    _, (d_write, _) = pick_kernel(counter_per_dispatch(write_dir, "WRITE_SIZE"),
+                                  "decode_mfma_kernel")
+    f_read = n_copy / 1024.0 / c_fetch
+    f_write = n_copy / 1024.0 / c_write
+    read_b = d_fetch * 1024.0 * f_read
+    write_b = d_write * 1024.0 * f_write
+    rec = {
+        "kernel_source_hash": kernel_source_hash(),
+        "kernel": name[:name.index(">(") + 1] if ">(" in name else name,
+        "bytes_per_launch": round(read_b + write_b),
+        "read_bytes_per_launch": round(read_b),
+        "write_bytes_per_launch": round(write_b),
+        "fetch_size_kib_per_dispatch": d_fetch,
+        "write_size_kib_per_dispatch": d_write,
+        "dispatches": nd,
+        "copy_bytes": n_copy,
+        "copy_fetch_size_kib": c_fetch,
+        "copy_write_size_kib": c_write,
+        "scale_read": f_read,
+        "scale_write": f_write,
+    }
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    table[workload] = rec
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+    print(json.dumps(rec))
+    return rec
+
+
 def main():
     args = parse()
+    if args.ingest_counters:
+        ingest_counters(args.ingest_counters, args.workload)
+        return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; "
-                          "--gpus must be 1 (see DESIGN.md for how the path "
-                          "would shard)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark measures one GPU: --gpus must be 1",
+                          "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
     if args.copy_calibration:
@@ -124,6 +204,14 @@ def main():
         vp, kp = pools[i % R]
         gva.decode_attention(qa, vp, kp, x["block_table"], x["seq_lens"],
                              x["max_seq_len"], workspace=ws, out=out, lse=lse)
+
+    if args.decode_only:  # decode launches alone, eager, over the rotating copies
+        for i in range(args.warmup + args.steps):
+            decode_only(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"decode_only": cfg.name, "launches": args.warmup + args.steps,
+                          "algorithmic_bytes_per_launch": cache_bytes}))
+        return
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):

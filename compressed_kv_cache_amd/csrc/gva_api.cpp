@@ -178,7 +178,7 @@ const char* gva_status_string(int32_t status) {
     case GVA_OK: return "ok";
     case GVA_ERR_NULL: return "a required pointer is NULL";
     case GVA_ERR_SHAPE: return "invalid or inconsistent sizes";
-    case GVA_ERR_UNSUPPORTED: return "sizes not supported by this build";
+    case GVA_ERR_UNSUPPORTED: return "sizes the library has no kernel for";
     case GVA_ERR_ALIGN: return "pointer not 16-byte aligned";
     case GVA_ERR_WORKSPACE: return "workspace too small";
     case GVA_ERR_HIP: return "HIP runtime error";

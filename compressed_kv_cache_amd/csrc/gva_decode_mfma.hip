@@ -156,7 +156,7 @@ struct WaveCtx {
   const bf16_t* k_base;    // k_pool (GQA: + group g0 + 8*q4)
   const int32_t* bt_row;   // block_table row of this sequence
   size_t vrow;             // elements per value (or key) row
-  int num_blocks, j_begin, j_end, q4, li, lg;
+  int num_blocks, max_blocks, j_begin, j_end, q4, li, lg;
   unsigned char* lds;      // this wave's LDS tile (2 x 16 rows)
 };
 
@@ -170,16 +170,16 @@ template <int GT, int DH, int DR, bool GQA>
 __device__ __forceinline__ void load_tile(const WaveCtx& w, int k, int n_tiles,
                                           TileRegs<GT, DH, DR, GQA>& t, int& bad) {
   using C = Cfg<GT, DH, DR, GQA>;
-  size_t row = 0;
-  if (k < n_tiles) {  // uniform
-    const int j0 = w.j_begin + kTileTok * k;
-    int blk = w.bt_row[j0 / kBlock];
-    if (static_cast<unsigned>(blk) >= static_cast<unsigned>(w.num_blocks)) {
-      bad = 1;
-      blk = 0;  // stay in bounds; the chunk is reported NaN
-    }
-    row = static_cast<size_t>(blk) * kBlock + (j0 % kBlock) + w.li;
-  }
+  // branch-free, so the loads stay in the caller's basic block and issue
+  // where the caller put them: the block-table entry is read at a clamped
+  // index, and a tile past the end, or a bad entry, maps to row 0
+  const bool real = k < n_tiles;  // uniform
+  const int j0 = w.j_begin + kTileTok * k;
+  const int blk = w.bt_row[min(j0 / kBlock, w.max_blocks - 1)];
+  const bool in_pool = static_cast<unsigned>(blk) < static_cast<unsigned>(w.num_blocks);
+  bad |= (real && !in_pool) ? 1 : 0;  // the chunk is reported NaN
+  const size_t row =
+      (real && in_pool) ? static_cast<size_t>(blk) * kBlock + (j0 % kBlock) + w.li : 0;
   const bf16_t* vr = w.v_base + row * w.vrow;
 #pragma unroll
   for (int g = 0; g < GT; ++g)
@@ -315,6 +315,38 @@ __device__ __forceinline__ void softmax_pv(const WaveCtx& w, int cntA, int cntB,
   wave_lds_fence();
 }
 
+// Tile-pair step on the sets (x, y) holding tiles kx < ky: the scores and
+// LDS staging of each tile, each set reloaded with its next tile (nx, ny;
+// ny < 0: no reload) as soon as its scores are taken, then the softmax and
+// P.V update.
+template <int GT, int DH, int DR, bool GQA>
+__device__ __forceinline__ void pair_step(const WaveCtx& w, const QOps<GT, DH, DR, GQA>& qo,
+                                          SoftState<GT, DH, DR, GQA>& st, int n_tiles, int& bad,
+                                          TileRegs<GT, DH, DR, GQA>& x,
+                                          TileRegs<GT, DH, DR, GQA>& y, int kx, int ky, int nx,
+                                          int ny) {
+  const int cx = max(0, min(kTileTok, w.j_end - (w.j_begin + kTileTok * kx)));
+  const int cy = max(0, min(kTileTok, w.j_end - (w.j_begin + kTileTok * ky)));
+  const f32x4 sa = score_and_stage(w, cx, x, qo, 0);
+  load_tile(w, nx, n_tiles, x, bad);
+  const f32x4 sb = score_and_stage(w, cy, y, qo, 1);
+  if (ny >= 0) load_tile(w, ny, n_tiles, y, bad);
+  softmax_pv(w, cx, cy, sa, sb, st);
+}
+
+// The final step: no reloads.
+template <int GT, int DH, int DR, bool GQA>
+__device__ __forceinline__ void last_step(const WaveCtx& w, const QOps<GT, DH, DR, GQA>& qo,
+                                          SoftState<GT, DH, DR, GQA>& st,
+                                          const TileRegs<GT, DH, DR, GQA>& x,
+                                          const TileRegs<GT, DH, DR, GQA>& y, int kx, int ky) {
+  const int cx = max(0, min(kTileTok, w.j_end - (w.j_begin + kTileTok * kx)));
+  const int cy = max(0, min(kTileTok, w.j_end - (w.j_begin + kTileTok * ky)));
+  const f32x4 sa = score_and_stage(w, cx, x, qo, 0);
+  const f32x4 sb = score_and_stage(w, cy, y, qo, 1);
+  softmax_pv(w, cx, cy, sa, sb, st);
+}
+
 // NW: waves per block.  WPE: waves per SIMD the register budget is sized
 // for (2 where the tiles fit in 256 registers without spilling, else 1).
 // NSET: register tile sets in rotation (3, or 2 where three would spill).
@@ -366,6 +398,7 @@ void decode_mfma_kernel(
   w.k_base = GQA ? k_pool + static_cast<size_t>(g0) * DH + 8 * q4 : k_pool;
   w.bt_row = block_table + static_cast<size_t>(b) * max_blocks;
   w.num_blocks = num_blocks;
+  w.max_blocks = max_blocks;
   w.j_begin = j_begin;
   w.j_end = j_end;
   w.q4 = q4;
@@ -413,61 +446,50 @@ void decode_mfma_kernel(
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) st.acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- main loop: this wave's tiles sub + i*nsub, two per step; three
-  // register sets rotate so the next loads go out as soon as a set is free.
+  // ---- main loop: tiles of 16 tokens, two per step.  Each wave starts on
+  // tiles sub, sub + nsub (, sub + 2 nsub) and then takes the next free tile
+  // of its head tile from an LDS counter when a register set frees up, so
+  // waves whose data arrives first take more tiles and all waves of a block
+  // finish together.  A wave's tile indices increase in the order its sets
+  // are loaded, and the sets are consumed in that order, so the first index
+  // at or past n_tiles ends the wave's loop.
   {
+    // This wave's tiles are sub, sub + nsub, ... (n_my of them), taken two
+    // per step.  Full rounds of three steps run in a counted loop and the
+    // last one or two steps follow it: a loop with exits in its middle would
+    // re-enter its head through a merged block, and the compiler then waits
+    // there for every load in flight.  Loads of tiles past n_my read pool
+    // row 0 and are never used.
+    const int n_my = sub < n_tiles ? (n_tiles - sub + nsub - 1) / nsub : 0;
+    const int n_steps = (n_my + 1) / 2;
     auto tile = [&](int i) { return sub + i * nsub; };
-    auto count = [&](int i) {
-      return max(0, min(kTileTok, j_end - (j_begin + kTileTok * tile(i))));
-    };
     if constexpr (NSET == 3) {
       TileRegs<GT, DH, DR, GQA> ta, tb, tc;
       load_tile(w, tile(0), n_tiles, ta, bad);
       load_tile(w, tile(1), n_tiles, tb, bad);
       load_tile(w, tile(2), n_tiles, tc, bad);
       int i = 0;
-      while (tile(i) < n_tiles) {
-        // pair (i, i+1) in (ta, tb)
-        {
-          const f32x4 sa = score_and_stage(w, count(i), ta, qo, 0);
-          load_tile(w, tile(i + 3), n_tiles, ta, bad);
-          const f32x4 sb = score_and_stage(w, count(i + 1), tb, qo, 1);
-          load_tile(w, tile(i + 4), n_tiles, tb, bad);
-          softmax_pv(w, count(i), count(i + 1), sa, sb, st);
-        }
-        i += 2;
-        if (tile(i) >= n_tiles) break;
-        // pair (i, i+1) in (tc, ta)
-        {
-          const f32x4 sa = score_and_stage(w, count(i), tc, qo, 0);
-          load_tile(w, tile(i + 3), n_tiles, tc, bad);
-          const f32x4 sb = score_and_stage(w, count(i + 1), ta, qo, 1);
-          load_tile(w, tile(i + 4), n_tiles, ta, bad);
-          softmax_pv(w, count(i), count(i + 1), sa, sb, st);
-        }
-        i += 2;
-        if (tile(i) >= n_tiles) break;
-        // pair (i, i+1) in (tb, tc)
-        {
-          const f32x4 sa = score_and_stage(w, count(i), tb, qo, 0);
-          load_tile(w, tile(i + 3), n_tiles, tb, bad);
-          const f32x4 sb = score_and_stage(w, count(i + 1), tc, qo, 1);
-          load_tile(w, tile(i + 4), n_tiles, tc, bad);
-          softmax_pv(w, count(i), count(i + 1), sa, sb, st);
-        }
-        i += 2;
+      for (int r = 0; r < n_steps / 3; ++r, i += 6) {
+        pair_step(w, qo, st, n_tiles, bad, ta, tb, tile(i), tile(i + 1), tile(i + 3), tile(i + 4));
+        pair_step(w, qo, st, n_tiles, bad, tc, ta, tile(i + 2), tile(i + 3), tile(i + 5),
+                  tile(i + 6));
+        pair_step(w, qo, st, n_tiles, bad, tb, tc, tile(i + 4), tile(i + 5), tile(i + 7),
+                  tile(i + 8));
+      }
+      const int rem = n_steps % 3;
+      if (rem == 1) {
+        last_step(w, qo, st, ta, tb, tile(i), tile(i + 1));
+      } else if (rem == 2) {
+        pair_step(w, qo, st, n_tiles, bad, ta, tb, tile(i), tile(i + 1), tile(i + 3), -1);
+        last_step(w, qo, st, tc, ta, tile(i + 2), tile(i + 3));
       }
     } else {
       TileRegs<GT, DH, DR, GQA> ta, tb;
       load_tile(w, tile(0), n_tiles, ta, bad);
       load_tile(w, tile(1), n_tiles, tb, bad);
-      for (int i = 0; tile(i) < n_tiles; i += 2) {
-        const f32x4 sa = score_and_stage(w, count(i), ta, qo, 0);
-        load_tile(w, tile(i + 2), n_tiles, ta, bad);
-        const f32x4 sb = score_and_stage(w, count(i + 1), tb, qo, 1);
-        load_tile(w, tile(i + 3), n_tiles, tb, bad);
-        softmax_pv(w, count(i), count(i + 1), sa, sb, st);
-      }
+      for (int i = 0; i < 2 * n_steps; i += 2)
+        pair_step(w, qo, st, n_tiles, bad, ta, tb, tile(i), tile(i + 1), tile(i + 2),
+                  tile(i + 3));
     }
   }
 
@@ -493,20 +515,29 @@ void decode_mfma_kernel(
     const int hh = i / (DH / 4);          // head within the block's H
     const int d4 = (i % (DH / 4)) * 4;
     const int t_ht = hh / 16, n = hh % 16;
+    // the waves of head tile t_ht are t_ht, t_ht + nht, ...; all NW records
+    // are read at once and the others weighted out
+    float mv[NW], lv[NW];
+    float4 av[NW];
     float m_star = -INFINITY;
-    for (int wv = t_ht; wv < NW; wv += nht)
-      m_star = fmaxf(m_star, all[(wv * 16 + n) * C::REC]);
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv) {
+      const float* rr = all + (wv * 16 + n) * C::REC;
+      mv[wv] = (wv % nht == t_ht) ? rr[0] : -INFINITY;
+      lv[wv] = rr[1];
+      av[wv] = *reinterpret_cast<const float4*>(rr + 4 + d4);
+      m_star = fmaxf(m_star, mv[wv]);
+    }
     float L = 0.f;
     float4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int wv = t_ht; wv < NW; wv += nht) {
-      const float* rr = all + (wv * 16 + n) * C::REC;
-      const float wt = exp2f(rr[0] - m_star);
-      L = fmaf(wt, rr[1], L);
-      const float4 a = *reinterpret_cast<const float4*>(rr + 4 + d4);
-      o.x = fmaf(wt, a.x, o.x);
-      o.y = fmaf(wt, a.y, o.y);
-      o.z = fmaf(wt, a.z, o.z);
-      o.w = fmaf(wt, a.w, o.w);
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv) {
+      const float wt = (mv[wv] == -INFINITY) ? 0.f : exp2f(mv[wv] - m_star);
+      L = fmaf(wt, lv[wv], L);
+      o.x = fmaf(wt, av[wv].x, o.x);
+      o.y = fmaf(wt, av[wv].y, o.y);
+      o.z = fmaf(wt, av[wv].z, o.z);
+      o.w = fmaf(wt, av[wv].w, o.w);
     }
     float* dst = pb + hh * C::REC;
     store_dev2(dst + 4 + d4, o.x, o.y);
@@ -543,17 +574,15 @@ void decode_mfma_kernel(
     for (int c0 = 0; c0 < nc; c0 += U) {
       float2 ml[U], a[U], bb[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (c0 + u < nc) {
-          const float* r = r0 + (c0 + u) * cstride;
-          ml[u] = load_dev2(r);
-          a[u] = load_dev2(r + 4 + d4);
-          bb[u] = load_dev2(r + 6 + d4);
-        } else {
-          ml[u] = float2{-INFINITY, 0.f};
-          a[u] = bb[u] = float2{0.f, 0.f};
-        }
+      for (int u = 0; u < U; ++u) {  // past the last chunk: reload it, weight 0
+        const float* r = r0 + min(c0 + u, nc - 1) * cstride;
+        ml[u] = load_dev2(r);
+        a[u] = load_dev2(r + 4 + d4);
+        bb[u] = load_dev2(r + 6 + d4);
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (c0 + u >= nc) ml[u] = float2{-INFINITY, 0.f};
       float m_new = m_run;
 #pragma unroll
       for (int u = 0; u < U; ++u) m_new = fmaxf(m_new, ml[u].x);

@@ -58,7 +58,7 @@ typedef enum gva_status {
   GVA_OK = 0,
   GVA_ERR_NULL = 1,        /* a required pointer is NULL                    */
   GVA_ERR_SHAPE = 2,       /* a size is non-positive or sizes disagree      */
-  GVA_ERR_UNSUPPORTED = 3, /* valid sizes this build has no kernel for      */
+  GVA_ERR_UNSUPPORTED = 3, /* valid sizes the library has no kernel for    */
   GVA_ERR_ALIGN = 4,       /* a 16B pointer is not 16-byte aligned          */
   GVA_ERR_WORKSPACE = 5,   /* workspace smaller than the size query returns */
   GVA_ERR_HIP = 6          /* the HIP runtime rejected a launch             */

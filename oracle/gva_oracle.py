@@ -27,7 +27,7 @@ key ``K_h = V_g(h) M_h`` and runs a textbook softmax over the full keys
 evaluation (``absorb_query`` + ``attend_absorbed``) is a separate definition
 used to pin Eq. 7 and to test the library's separate entry points.
 
-Readings of points the pages leave open (each listed in the design doc):
+Readings of points the pages leave open:
 
 * softmax scale: 1/sqrt(d_n + d_r), the width of the full query/key;
 * head -> group map g(h) = h // (H/G) (contiguous groups);
