@@ -83,6 +83,26 @@ __device__ __forceinline__ int lds_off(int row, int chunk, int ROWB) {
   return row * ROWB + ((chunk ^ swz(row)) << 4);
 }
 
+// GVA tiles are read in 1 KB pieces: piece x of a wave covers bytes
+// [1024 x, 1024 x + 1024) of its tile slice (16 rows of ROWB bytes, the
+// wave's value groups), lane l taking 16 bytes at 1024 x + 16 l.  Every load
+// instruction thus reads whole 128-byte lines (reading the MFMA operand
+// layout, 16 rows x 64 bytes, straight from memory fetches every line in two
+// halves).  The pieces are written to LDS and the operands read back there.
+// The lane's part (row and 16-byte chunk within the first piece) is the same
+// for every piece; piece x adds x*1024/ROWB rows (ROWB <= 1024) or, for wider
+// rows, row x/(ROWB/1024) and 64*(x % (ROWB/1024)) chunks.
+template <int ROWB>
+__device__ __forceinline__ int lane_row(int lane) { return ROWB <= 1024 ? (16 * lane) / ROWB : 0; }
+template <int ROWB>
+__device__ __forceinline__ int lane_chunk(int lane) {
+  return ROWB <= 1024 ? ((16 * lane) % ROWB) >> 4 : lane;
+}
+template <int ROWB>
+constexpr int piece_row(int x) { return ROWB <= 1024 ? x * (1024 / ROWB) : x / (ROWB / 1024); }
+template <int ROWB>
+constexpr int piece_chunk(int x) { return ROWB <= 1024 ? 0 : 64 * (x % (ROWB / 1024)); }
+
 __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -153,10 +173,13 @@ struct SoftState {
 // Per-wave constants.
 struct WaveCtx {
   const bf16_t* v_base;    // v_pool + group g0 + 8*q4 (row 0)
+  const bf16_t* v_tile;    // v_pool + group g0 (row 0)
   const bf16_t* k_base;    // k_pool (GQA: + group g0 + 8*q4)
   const int32_t* bt_row;   // block_table row of this sequence
   size_t vrow;             // elements per value (or key) row
   int num_blocks, max_blocks, j_begin, j_end, q4, li, lg;
+  int lrow, lchunk;        // GVA pieces: this lane's row and chunk in piece 0
+  unsigned loff;           // ... and its byte offset from the piece's base
   unsigned char* lds;      // this wave's LDS tile (2 x 16 rows)
 };
 
@@ -178,21 +201,30 @@ __device__ __forceinline__ void load_tile(const WaveCtx& w, int k, int n_tiles,
   const int blk = w.bt_row[min(j0 / kBlock, w.max_blocks - 1)];
   const bool in_pool = static_cast<unsigned>(blk) < static_cast<unsigned>(w.num_blocks);
   bad |= (real && !in_pool) ? 1 : 0;  // the chunk is reported NaN
-  const size_t row =
-      (real && in_pool) ? static_cast<size_t>(blk) * kBlock + (j0 % kBlock) + w.li : 0;
-  const bf16_t* vr = w.v_base + row * w.vrow;
-#pragma unroll
-  for (int g = 0; g < GT; ++g)
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s) t.v[g * C::KS + s] = stream_load16(vr + g * DH + 32 * s);
+  const size_t row0 = (real && in_pool) ? static_cast<size_t>(blk) * kBlock + (j0 % kBlock) : 0;
   if constexpr (GQA) {
+    const size_t row = row0 + w.li;
+    const bf16_t* vr = w.v_base + row * w.vrow;
     const bf16_t* kr = w.k_base + row * w.vrow;
 #pragma unroll
     for (int g = 0; g < GT; ++g)
 #pragma unroll
-      for (int s = 0; s < C::KS; ++s) t.k[g * C::KS + s] = stream_load16(kr + g * DH + 32 * s);
+      for (int s = 0; s < C::KS; ++s) {
+        t.v[g * C::KS + s] = stream_load16(vr + g * DH + 32 * s);
+        t.k[g * C::KS + s] = stream_load16(kr + g * DH + 32 * s);
+      }
   } else {
-    const bf16_t* kr = w.k_base + row * DR;
+    static_assert(C::ROWB % 1024 == 0 || 1024 % C::ROWB == 0, "piece layout");
+    // uniform base per piece + one per-lane byte offset
+    const unsigned char* tile = reinterpret_cast<const unsigned char*>(w.v_tile + row0 * w.vrow);
+    const size_t rstride = w.vrow * sizeof(bf16_t);
+#pragma unroll
+    for (int x = 0; x < C::NV; ++x) {
+      const unsigned char* pb =
+          tile + piece_row<C::ROWB>(x) * rstride + 16 * piece_chunk<C::ROWB>(x);
+      t.v[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pb + w.loff));
+    }
+    const bf16_t* kr = w.k_base + (row0 + w.li) * DR;
 #pragma unroll
     for (int s = 0; s < C::NR; ++s) {
       // lanes past d_r read an in-row address; their query slots are zero
@@ -203,26 +235,65 @@ __device__ __forceinline__ void load_tile(const WaveCtx& w, int k, int n_tiles,
 }
 
 // Scores of one 16-token tile for this lane's head (tokens 4*q4 .. +3 in
-// log2 units), and the tile's value rows copied into LDS half `half`.
-// Rows past the sequence end carry whatever the slot holds: the caller
-// masks their scores, and their LDS copy is zero.
+// log2 units), and the tile's value rows copied into LDS half `half`
+// (GVA: copied first, and the score operands read back from LDS).  Rows
+// past the sequence end carry whatever the slot holds: the caller masks
+// their scores, and their LDS copy is zero.
 template <int GT, int DH, int DR, bool GQA>
 __device__ __forceinline__ f32x4 score_and_stage(const WaveCtx& w, int cnt,
                                                  const TileRegs<GT, DH, DR, GQA>& t,
                                                  const QOps<GT, DH, DR, GQA>& qo, int half) {
   using C = Cfg<GT, DH, DR, GQA>;
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
   f32x4 sg[GT];
+  if constexpr (GQA) {
 #pragma unroll
-  for (int g = 0; g < GT; ++g) {
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < GT; ++g) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      const bf16x8 op =
-          __builtin_bit_cast(bf16x8, GQA ? t.k[g * C::KS + s] : t.v[g * C::KS + s]);
-      a = mfma32(op, qo.qh[s], a);
-      a = mfma32(op, qo.ql[s], a);
+      for (int s = 0; s < C::KS; ++s) {
+        const bf16x8 op = __builtin_bit_cast(bf16x8, t.k[g * C::KS + s]);
+        a = mfma32(op, qo.qh[s], a);
+        a = mfma32(op, qo.ql[s], a);
+      }
+      sg[g] = a;
     }
-    sg[g] = a;
+    wave_lds_fence();
+    const int row = 16 * half + w.li;
+    const bool valid = w.li < cnt;
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) {
+        const int chunk = g * (DH / 8) + 4 * s + w.q4;
+        *reinterpret_cast<u32x4*>(w.lds + lds_off(row, chunk, C::ROWB)) =
+            valid ? t.v[g * C::KS + s] : z4;
+      }
+  } else {
+    // stage the pieces (rows past the end as zeros), then read the operands
+    wave_lds_fence();
+#pragma unroll
+    for (int x = 0; x < C::NV; ++x) {
+      const int r = w.lrow + piece_row<C::ROWB>(x);
+      const int c = w.lchunk + piece_chunk<C::ROWB>(x);
+      *reinterpret_cast<u32x4*>(w.lds + lds_off(16 * half + r, c, C::ROWB)) =
+          r < cnt ? t.v[x] : z4;
+    }
+    wave_lds_fence();
+    const int row = 16 * half + w.li;
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) {
+        const int chunk = g * (DH / 8) + 4 * s + w.q4;
+        const bf16x8 op = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(w.lds + lds_off(row, chunk, C::ROWB)));
+        a = mfma32(op, qo.qh[s], a);
+        a = mfma32(op, qo.ql[s], a);
+      }
+      sg[g] = a;
+    }
   }
   f32x4 sc = sg[0];
 #pragma unroll
@@ -237,18 +308,6 @@ __device__ __forceinline__ f32x4 score_and_stage(const WaveCtx& w, int cnt,
     }
     sc += sr;
   }
-  wave_lds_fence();
-  const int row = 16 * half + w.li;
-  const bool valid = w.li < cnt;
-  const u32x4 z4 = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int g = 0; g < GT; ++g)
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      const int chunk = g * (DH / 8) + 4 * s + w.q4;
-      *reinterpret_cast<u32x4*>(w.lds + lds_off(row, chunk, C::ROWB)) =
-          valid ? t.v[g * C::KS + s] : z4;
-    }
   return sc;
 }
 
@@ -395,6 +454,7 @@ void decode_mfma_kernel(
   WaveCtx w;
   w.vrow = static_cast<size_t>(G) * DH;
   w.v_base = v_pool + static_cast<size_t>(g0) * DH + 8 * q4;
+  w.v_tile = v_pool + static_cast<size_t>(g0) * DH;
   w.k_base = GQA ? k_pool + static_cast<size_t>(g0) * DH + 8 * q4 : k_pool;
   w.bt_row = block_table + static_cast<size_t>(b) * max_blocks;
   w.num_blocks = num_blocks;
@@ -404,6 +464,9 @@ void decode_mfma_kernel(
   w.q4 = q4;
   w.li = li;
   w.lg = li / (16 / GT);
+  w.lrow = lane_row<C::ROWB>(lane);
+  w.lchunk = lane_chunk<C::ROWB>(lane);
+  w.loff = static_cast<unsigned>(w.lrow * G * DH * sizeof(bf16_t) + 16 * w.lchunk);
   w.lds = lds_raw + wave * C::WAVE_LDS;
 
   // ---- query operands: log2-scaled, split into bf16 hi + lo ----
@@ -622,7 +685,7 @@ hipError_t launch_one(const gva_shape& s, const DecodePlan& plan, const DecodeAr
   // 4 waves per block.
   constexpr int NW = (DH == 64 && !GQA) ? 8 : 4;
   constexpr int WPE = (DH == 64 && !GQA) ? 2 : 1;
-  constexpr int NSET = (DH == 128 && GQA) ? 2 : 3;
+  constexpr int NSET = GQA && DH == 64 ? 3 : 2;
   if ((s.H / 16) > NW || NW % (s.H / 16) != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL((decode_mfma_kernel<GT, DH, DR, GQA, NW, WPE, NSET>), grid, dim3(64 * NW),
                      0, stream,
