@@ -376,9 +376,11 @@ __device__ __forceinline__ void softmax_pv(const WaveCtx& w, int cntA, int cntB,
 
 // Tile-pair step on the sets (x, y) holding tiles kx < ky: the scores and
 // LDS staging of each tile, each set reloaded with its next tile (nx, ny;
-// ny < 0: no reload) as soon as its scores are taken, then the softmax and
-// P.V update.
-template <int GT, int DH, int DR, bool GQA>
+// y only if RELOAD_Y) as soon as its scores are taken, then the softmax and
+// P.V update.  RELOAD_Y is a template flag: a branch around the reload
+// would make the compiler assume, at the loop head, that y has nothing in
+// flight, and wait there for every load.
+template <bool RELOAD_Y = true, int GT, int DH, int DR, bool GQA>
 __device__ __forceinline__ void pair_step(const WaveCtx& w, const QOps<GT, DH, DR, GQA>& qo,
                                           SoftState<GT, DH, DR, GQA>& st, int n_tiles, int& bad,
                                           TileRegs<GT, DH, DR, GQA>& x,
@@ -388,8 +390,11 @@ __device__ __forceinline__ void pair_step(const WaveCtx& w, const QOps<GT, DH, D
   const int cy = max(0, min(kTileTok, w.j_end - (w.j_begin + kTileTok * ky)));
   const f32x4 sa = score_and_stage(w, cx, x, qo, 0);
   load_tile(w, nx, n_tiles, x, bad);
+  // keep the scheduler from moving y's staging (which waits for y's data)
+  // above x's reload: the reload must go out while y is still in flight
+  __builtin_amdgcn_sched_barrier(0);
   const f32x4 sb = score_and_stage(w, cy, y, qo, 1);
-  if (ny >= 0) load_tile(w, ny, n_tiles, y, bad);
+  if constexpr (RELOAD_Y) load_tile(w, ny, n_tiles, y, bad);
   softmax_pv(w, cx, cy, sa, sb, st);
 }
 
@@ -543,7 +548,7 @@ void decode_mfma_kernel(
       if (rem == 1) {
         last_step(w, qo, st, ta, tb, tile(i), tile(i + 1));
       } else if (rem == 2) {
-        pair_step(w, qo, st, n_tiles, bad, ta, tb, tile(i), tile(i + 1), tile(i + 3), -1);
+        pair_step<false>(w, qo, st, n_tiles, bad, ta, tb, tile(i), tile(i + 1), tile(i + 3), 0);
         last_step(w, qo, st, tc, ta, tile(i + 2), tile(i + 3));
       }
     } else {
