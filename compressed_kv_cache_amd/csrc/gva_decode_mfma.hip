@@ -174,6 +174,7 @@ struct SoftState {
 struct WaveCtx {
   const bf16_t* v_base;    // v_pool + group g0 + 8*q4 (row 0)
   const bf16_t* v_tile;    // v_pool + group g0 (row 0)
+  const bf16_t* k_tile;    // GQA: k_pool + group g0 (row 0)
   const bf16_t* k_base;    // k_pool (GQA: + group g0 + 8*q4)
   const int32_t* bt_row;   // block_table row of this sequence
   size_t vrow;             // elements per value (or key) row
@@ -203,16 +204,15 @@ __device__ __forceinline__ void load_tile(const WaveCtx& w, int k, int n_tiles,
   bad |= (real && !in_pool) ? 1 : 0;  // the chunk is reported NaN
   const size_t row0 = (real && in_pool) ? static_cast<size_t>(blk) * kBlock + (j0 % kBlock) : 0;
   if constexpr (GQA) {
-    const size_t row = row0 + w.li;
-    const bf16_t* vr = w.v_base + row * w.vrow;
-    const bf16_t* kr = w.k_base + row * w.vrow;
+    const unsigned char* vt = reinterpret_cast<const unsigned char*>(w.v_tile + row0 * w.vrow);
+    const unsigned char* kt = reinterpret_cast<const unsigned char*>(w.k_tile + row0 * w.vrow);
+    const size_t rstride = w.vrow * sizeof(bf16_t);
 #pragma unroll
-    for (int g = 0; g < GT; ++g)
-#pragma unroll
-      for (int s = 0; s < C::KS; ++s) {
-        t.v[g * C::KS + s] = stream_load16(vr + g * DH + 32 * s);
-        t.k[g * C::KS + s] = stream_load16(kr + g * DH + 32 * s);
-      }
+    for (int x = 0; x < C::NV; ++x) {
+      const size_t o = piece_row<C::ROWB>(x) * rstride + 16 * piece_chunk<C::ROWB>(x) + w.loff;
+      t.v[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vt + o));
+      t.k[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + o));
+    }
   } else {
     static_assert(C::ROWB % 1024 == 0 || 1024 % C::ROWB == 0, "piece layout");
     // uniform base per piece + one per-lane byte offset
@@ -247,28 +247,37 @@ __device__ __forceinline__ f32x4 score_and_stage(const WaveCtx& w, int cnt,
   const u32x4 z4 = {0u, 0u, 0u, 0u};
   f32x4 sg[GT];
   if constexpr (GQA) {
+    // keys through the LDS half first (score operands), then the values
+    wave_lds_fence();
+#pragma unroll
+    for (int x = 0; x < C::NV; ++x) {
+      const int r = w.lrow + piece_row<C::ROWB>(x);
+      const int c = w.lchunk + piece_chunk<C::ROWB>(x);
+      *reinterpret_cast<u32x4*>(w.lds + lds_off(16 * half + r, c, C::ROWB)) = t.k[x];
+    }
+    wave_lds_fence();
+    const int row = 16 * half + w.li;
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < C::KS; ++s) {
-        const bf16x8 op = __builtin_bit_cast(bf16x8, t.k[g * C::KS + s]);
+        const int chunk = g * (DH / 8) + 4 * s + w.q4;
+        const bf16x8 op = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(w.lds + lds_off(row, chunk, C::ROWB)));
         a = mfma32(op, qo.qh[s], a);
         a = mfma32(op, qo.ql[s], a);
       }
       sg[g] = a;
     }
     wave_lds_fence();
-    const int row = 16 * half + w.li;
-    const bool valid = w.li < cnt;
 #pragma unroll
-    for (int g = 0; g < GT; ++g)
-#pragma unroll
-      for (int s = 0; s < C::KS; ++s) {
-        const int chunk = g * (DH / 8) + 4 * s + w.q4;
-        *reinterpret_cast<u32x4*>(w.lds + lds_off(row, chunk, C::ROWB)) =
-            valid ? t.v[g * C::KS + s] : z4;
-      }
+    for (int x = 0; x < C::NV; ++x) {
+      const int r = w.lrow + piece_row<C::ROWB>(x);
+      const int c = w.lchunk + piece_chunk<C::ROWB>(x);
+      *reinterpret_cast<u32x4*>(w.lds + lds_off(16 * half + r, c, C::ROWB)) =
+          r < cnt ? t.v[x] : z4;
+    }
   } else {
     // stage the pieces (rows past the end as zeros), then read the operands
     wave_lds_fence();
@@ -460,6 +469,7 @@ void decode_mfma_kernel(
   w.vrow = static_cast<size_t>(G) * DH;
   w.v_base = v_pool + static_cast<size_t>(g0) * DH + 8 * q4;
   w.v_tile = v_pool + static_cast<size_t>(g0) * DH;
+  w.k_tile = k_pool + static_cast<size_t>(g0) * DH;
   w.k_base = GQA ? k_pool + static_cast<size_t>(g0) * DH + 8 * q4 : k_pool;
   w.bt_row = block_table + static_cast<size_t>(b) * max_blocks;
   w.num_blocks = num_blocks;
