@@ -146,6 +146,9 @@ EDGE_LENS = [1, 2, 63, 64, 65, 127, 128, 129, 1000]
     (32, 8, 128, 96, 32),
     (16, 4, 64, 40, 24),
     (16, 2, 64, 62, 2),
+    (16, 4, 64, 32, 32),     # matrix cores: d_h 64, d_r 32
+    (16, 4, 128, 112, 16),   # matrix cores: d_h 128, d_r 16
+    (64, 16, 64, 48, 16),    # matrix cores: four head tiles per block
 ])
 def test_ragged_edges(g, gpu, shape, dtype):
     H, G, d_h, d_n, d_r = shape
@@ -394,3 +397,49 @@ def test_decode_step_without_append(g, gpu):
                            x["block_table"], x["seq_lens"], x["max_seq_len"])
     _, out2, _ = run_step(g, x, cfg)
     assert torch.equal(out, out2)
+
+
+# ------------------------------------------------------- split extremes ----
+
+def test_one_long_sequence_many_chunks(g, gpu):
+    """One sequence split over ~256 chunks: the final merge runs many rounds."""
+    cfg = syn.with_overrides(syn.get_config("decode_350m"), B=1, T=70000)
+    x, h = gen(cfg, gpu)
+    announce("one long sequence", cfg.T)
+    qa, out, lse = run_step(g, x, cfg)
+    ref, ref_lse = o.gva_decode_materialized(
+        h["q_nope"], h["q_rope"], h["M"], h["v_pool"], h["k_pool"], h["block_table"],
+        h["seq_lens"], base=cfg.rope_base)
+    assert_bf16_parity(cpu(out).double().numpy(), ref)
+    np.testing.assert_allclose(cpu(lse).double().numpy(), ref_lse, atol=1e-3)
+
+
+def test_more_sequences_than_split_target(g, gpu):
+    """B = 300 short sequences (more than the ~256 chunks aimed for)."""
+    cfg = syn.with_overrides(syn.get_config("decode_350m"), B=300, T=None,
+                             len_range=(1, 200))
+    x, h = gen(cfg, gpu)
+    announce("B=300")
+    qa, out, lse = run_step(g, x, cfg)
+    ref, ref_lse = o.gva_decode_materialized(
+        h["q_nope"], h["q_rope"], h["M"], h["v_pool"], h["k_pool"], h["block_table"],
+        h["seq_lens"], base=cfg.rope_base)
+    assert_bf16_parity(cpu(out).double().numpy(), ref)
+    np.testing.assert_allclose(cpu(lse).double().numpy(), ref_lse, atol=1e-3)
+
+
+@pytest.mark.parametrize("H,G,d_h", [(16, 4, 64), (32, 8, 128)])
+def test_gqa_ragged_edges(g, gpu, H, G, d_h):
+    base = syn.get_config("long_ragged")
+    cfg = syn.with_overrides(base, B=len(EDGE_LENS), H=H, G=G, d_h=d_h, d_n=d_h - 16,
+                             d_r=16, len_range=None, T=None)
+    lens = torch.tensor(EDGE_LENS, dtype=torch.int32)
+    y = syn.make_gqa_inputs(cfg, device=gpu, seq_lens=lens)  # shuffled block table
+    announce("gqa ragged edges", H, G, d_h)
+    out, lse = g.gqa_decode_attention(y["q"], y["k_pool"], y["v_pool"], y["block_table"],
+                                      y["seq_lens"], y["max_seq_len"])
+    h = {k: cpu(v) for k, v in y.items() if isinstance(v, torch.Tensor)}
+    ref, ref_lse = o.gqa_decode(h["q"], h["k_pool"], h["v_pool"], h["block_table"],
+                                h["seq_lens"])
+    assert_bf16_parity(cpu(out).double().numpy(), ref)
+    np.testing.assert_allclose(cpu(lse).double().numpy(), ref_lse, atol=1e-3)
