@@ -575,11 +575,13 @@ void decode_mfma_kernel(
   float l_run = st.l;
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  bad = __syncthreads_or(bad);
+  // waves still reading their tiles' LDS (P.V) finish before it is reused
+  __syncthreads();
   float* red = reinterpret_cast<float*>(lds_raw) + wave * 16 * C::REC;
   if (q4 == 0) {
     red[li * C::REC] = st.m;
     red[li * C::REC + 1] = l_run;
+    red[li * C::REC + 2] = __int_as_float(bad);  // any wave's bad entry taints the chunk
   }
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
@@ -598,11 +600,13 @@ void decode_mfma_kernel(
     float mv[NW], lv[NW];
     float4 av[NW];
     float m_star = -INFINITY;
+    int any_bad = 0;
 #pragma unroll
     for (int wv = 0; wv < NW; ++wv) {
       const float* rr = all + (wv * 16 + n) * C::REC;
       mv[wv] = (wv % nht == t_ht) ? rr[0] : -INFINITY;
       lv[wv] = rr[1];
+      any_bad |= __float_as_int(rr[2]);
       av[wv] = *reinterpret_cast<const float4*>(rr + 4 + d4);
       m_star = fmaxf(m_star, mv[wv]);
     }
@@ -610,7 +614,7 @@ void decode_mfma_kernel(
     float4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int wv = 0; wv < NW; ++wv) {
-      const float wt = (mv[wv] == -INFINITY) ? 0.f : exp2f(mv[wv] - m_star);
+      const float wt = (mv[wv] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv[wv] - m_star);
       L = fmaf(wt, lv[wv], L);
       o.x = fmaf(wt, av[wv].x, o.x);
       o.y = fmaf(wt, av[wv].y, o.y);
@@ -620,7 +624,7 @@ void decode_mfma_kernel(
     float* dst = pb + hh * C::REC;
     store_dev2(dst + 4 + d4, o.x, o.y);
     store_dev2(dst + 6 + d4, o.z, o.w);
-    if (d4 == 0) store_dev2(dst, m_star, bad ? nan : L);
+    if (d4 == 0) store_dev2(dst, m_star, any_bad ? nan : L);
   }
 
   // ---- the last block of this sequence merges its chunk records ----
@@ -664,7 +668,7 @@ void decode_mfma_kernel(
       float m_new = m_run;
 #pragma unroll
       for (int u = 0; u < U; ++u) m_new = fmaxf(m_new, ml[u].x);
-      const float sc = exp2f(m_run - m_new);
+      const float sc = __builtin_amdgcn_exp2f(m_run - m_new);
       L *= sc;
       o.x *= sc;
       o.y *= sc;
@@ -672,7 +676,7 @@ void decode_mfma_kernel(
       o.w *= sc;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float wt = exp2f(ml[u].x - m_new);
+        const float wt = __builtin_amdgcn_exp2f(ml[u].x - m_new);
         L = fmaf(wt, ml[u].y, L);
         o.x = fmaf(wt, a[u].x, o.x);
         o.y = fmaf(wt, a[u].y, o.y);
