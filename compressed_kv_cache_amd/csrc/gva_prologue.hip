@@ -41,6 +41,7 @@ struct PrologueArgs {
   int pos_offset;
   int B, H, G, d_h, d_n, d_r, bs, max_blocks, num_blocks;
   int absorb_blocks;   // blocks [0, absorb_blocks) absorb, the rest append
+  int vec4;            // q_nope and M rows 16-byte aligned (d_n % 4 == 0)
 };
 
 // Rotate (x0, x1) by angle pos * theta (float64).
@@ -82,25 +83,51 @@ __device__ __forceinline__ void absorb_block(const PrologueArgs& a, const RopeTa
   float x0 = xr[0], x1 = xr[1];
   int p_pos = a.pos[p_b] + a.pos_offset;
 
-  const int K4 = (a.d_n + 3) / 4;
   const int bq = min(b0 + li, a.B - 1);
   const float* qrow = a.q_nope + (static_cast<size_t>(bq) * a.H + h) * a.d_n;
   const float* mrow = a.M + (static_cast<size_t>(h) * a.d_h + et * 16 + li) * a.d_n;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < K4; s0 += kKBatch) {
-    float qv[kKBatch], mv[kKBatch];
+  if (a.vec4) {
+    // 16-byte loads: lane group kg sums n in [kg*K, kg*K + K), K a multiple
+    // of 4 (rows are 16-byte aligned and d_n % 4 == 0)
+    const int K = ((a.d_n + 15) / 16) * 4;
+    for (int s0 = 0; s0 < K; s0 += kKBatch) {
+      float4 qv[kKBatch / 4], mv[kKBatch / 4];
 #pragma unroll
-    for (int s = 0; s < kKBatch; ++s) {
-      const int n = kg * K4 + s0 + s;
-      const int nc = min(n, a.d_n - 1);
-      qv[s] = qrow[nc];
-      mv[s] = mrow[nc];
+      for (int j = 0; j < kKBatch / 4; ++j) {
+        const int n = min(kg * K + s0 + 4 * j, a.d_n - 4);  // in bounds, aligned
+        qv[j] = *reinterpret_cast<const float4*>(qrow + n);
+        mv[j] = *reinterpret_cast<const float4*>(mrow + n);
+      }
+#pragma unroll
+      for (int j = 0; j < kKBatch / 4; ++j) {
+        const int n = kg * K + s0 + 4 * j;
+        const bool ok = s0 + 4 * j < K && n < a.d_n;  // n < d_n implies n + 3 < d_n
+        const float q4v[4] = {qv[j].x, qv[j].y, qv[j].z, qv[j].w};
+        const float m4v[4] = {mv[j].x, mv[j].y, mv[j].z, mv[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ok ? q4v[e] : 0.f, ok ? m4v[e] : 0.f, acc,
+                                                     0, 0, 0);
+      }
     }
+  } else {
+    const int K4 = (a.d_n + 3) / 4;
+    for (int s0 = 0; s0 < K4; s0 += kKBatch) {
+      float qv[kKBatch], mv[kKBatch];
 #pragma unroll
-    for (int s = 0; s < kKBatch; ++s) {
-      const bool ok = (s0 + s < K4) && (kg * K4 + s0 + s < a.d_n);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ok ? qv[s] : 0.f, ok ? mv[s] : 0.f, acc, 0, 0,
-                                                 0);
+      for (int s = 0; s < kKBatch; ++s) {
+        const int n = kg * K4 + s0 + s;
+        const int nc = min(n, a.d_n - 1);
+        qv[s] = qrow[nc];
+        mv[s] = mrow[nc];
+      }
+#pragma unroll
+      for (int s = 0; s < kKBatch; ++s) {
+        const bool ok = (s0 + s < K4) && (kg * K4 + s0 + s < a.d_n);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ok ? qv[s] : 0.f, ok ? mv[s] : 0.f, acc, 0,
+                                                   0, 0);
+      }
     }
   }
 #pragma unroll
@@ -224,6 +251,8 @@ hipError_t launch_prologue(const gva_shape& s, const float* q_nope, const float*
   a.max_blocks = s.max_blocks;
   a.num_blocks = s.num_blocks;
   a.absorb_blocks = q_nope ? s.H * ((s.B + 15) / 16) * (s.d_h / 16) : 0;
+  a.vec4 = q_nope && s.d_n % 4 == 0 && reinterpret_cast<uintptr_t>(q_nope) % 16 == 0 &&
+           reinterpret_cast<uintptr_t>(M) % 16 == 0;
   const long long append_items =
       v_new ? static_cast<long long>(s.B) * (s.G * s.d_h / 4 + s.d_r / 2) : 0;
   const int blocks = a.absorb_blocks + static_cast<int>((append_items + kThreads - 1) / kThreads);
