@@ -229,26 +229,28 @@ def main():
     eager_ms = t0.elapsed_time(t1) / args.steps
     eager_out = out.clone()
 
-    # HIP graphs of R consecutive steps (one per rotating cache copy), and of
-    # R decode launches alone; replayed back to back.
+    S = max(R, 8)
+    # HIP graphs of S >= R consecutive steps (cycling over the rotating cache
+    # copies; at least 8 so graph launch costs stay small), and of S decode
+    # launches alone; replayed back to back.
     g_step, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for i in range(R):
+        for i in range(S):
             step(i)
     torch.cuda.current_stream().wait_stream(side)
     with torch.cuda.graph(g_step):
-        for i in range(R):
+        for i in range(S):
             step(i)
     with torch.cuda.graph(g_dec):
-        for i in range(R):
+        for i in range(S):
             decode_only(i)
     torch.cuda.synchronize()
     g_step.replay()
     torch.cuda.synchronize()
     graph_matches_eager = bool(torch.equal(out, eager_out))
-    reps = max(1, -(-args.steps // R))
+    reps = max(1, -(-args.steps // S))
     for _ in range(2):
         g_step.replay()
     torch.cuda.synchronize()
@@ -257,8 +259,8 @@ def main():
         g_step.replay()
     t1.record()
     torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / (reps * R)
-    steps_timed = reps * R
+    ms_per_step = t0.elapsed_time(t1) / (reps * S)
+    steps_timed = reps * S
 
     # decode launches alone: one event pair per graph of R launches
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -270,7 +272,7 @@ def main():
         g_dec.replay()
         evs[i][1].record()
     torch.cuda.synchronize()
-    dec_ms = sorted(a.elapsed_time(b) / R for a, b in evs)
+    dec_ms = sorted(a.elapsed_time(b) / S for a, b in evs)
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
     dec_med_ms = dec_ms[len(dec_ms) // 2]
     print(f"[bench] step {ms_per_step * 1e3:.2f} us (eager {eager_ms * 1e3:.2f} us), "
@@ -332,7 +334,7 @@ def main():
             "accumulate": "f32",
             "step": "gva_decode_step: append+absorb (1 launch) + decode with in-kernel merge "
                     "(1 launch)",
-            "timing": "HIP graph of R steps replayed back to back",
+            "timing": "HIP graphs of max(R, 8) steps replayed back to back",
             "rotating_cache_copies": R,
         },
         "roofline": {
@@ -369,16 +371,17 @@ def bench_gqa(torch, gva, syn, cfg, dev, steps, warmup):
         gva.gqa_decode_attention(y["q"], kp, vp, y["block_table"], y["seq_lens"],
                                  y["max_seq_len"], workspace=ws, out=out, lse=lse)
 
-    for i in range(max(warmup, R)):
+    S = max(R, 8)
+    for i in range(max(warmup, S)):
         launch(i)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for i in range(R):
+        for i in range(S):
             launch(i)
     g.replay()
     torch.cuda.synchronize()
-    reps = max(1, -(-steps // R))
+    reps = max(1, -(-steps // S))
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -386,7 +389,7 @@ def bench_gqa(torch, gva, syn, cfg, dev, steps, warmup):
         g.replay()
     t1.record()
     torch.cuda.synchronize()
-    avg = t0.elapsed_time(t1) / (reps * R)
+    avg = t0.elapsed_time(t1) / (reps * S)
     del pools, y
     torch.cuda.empty_cache()
     return {"us_avg": avg * 1e3, "cache_bytes": byts, "GBps": byts / (avg * 1e-3) / 1e9}
