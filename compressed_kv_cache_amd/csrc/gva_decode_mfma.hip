@@ -7,19 +7,20 @@
 // parts so the products carry ~16 mantissa bits; the cache values themselves
 // are exact bf16.
 //
-// Work split: block (c, b) owns chunk c of sequence b and runs 4 waves.
-// Query heads come in tiles of 16 (one MFMA column each); a head tile covers
-// GT = 16/(H/G) whole value groups.  With H/16 head tiles the waves are
-// divided between head tiles, and the waves of a head tile take the chunk's
-// 16-token tiles in turn.  A wave handles its tiles two at a time:
-//   1. each tile's value rows of its groups (and k_rope rows) come from HBM
-//      straight into MFMA A-operand registers (16 B per lane per k-step);
-//      three register sets rotate, so two tiles are in flight while one is
-//      consumed;
-//   2. scores S^T[token][head] = V_g . qa^T per group (16x16x32 MFMAs) plus
-//      k_rope . qr^T (16x16x16), keeping for each head its own group's sum;
-//   3. the tile's value rows go to a wave-private LDS tile (XOR-swizzled
-//      rows, conflict-free for the row writes and the transpose reads);
+// Work split: block (c, b) owns chunk c of sequence b and runs 8 waves
+// (d_h = 64) or 4 (d_h = 128, GQA).  Query heads come in tiles of 16 (one
+// MFMA column each); a head tile covers GT = 16/(H/G) whole value groups.
+// With H/16 head tiles the waves are divided between head tiles, and the
+// waves of a head tile take the chunk's 16-token tiles in turn, two per step:
+//   1. each tile's value rows of the wave's groups come from HBM in 1 KB
+//      pieces (16-byte loads covering whole 128-byte lines) and its k_rope
+//      rows into MFMA operand registers; two register sets alternate, each
+//      reloaded as soon as its tile is staged;
+//   2. the value rows go to a wave-private LDS tile (XOR-swizzled rows,
+//      conflict-free for the row writes and the transpose reads);
+//   3. scores S^T[token][head] = V_g . qa^T per group (16x16x32 MFMAs, V read
+//      back from LDS) plus k_rope . qr^T (16x16x16), keeping for each head
+//      its own group's sum;
 //   4. the running max/sum of each head absorb the pair's 32 scores (log2
 //      units); the max is raised only when a score exceeds it by 2^8, so the
 //      accumulator is rarely rescaled;
