@@ -27,6 +27,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -44,10 +45,15 @@ KERNEL_SOURCES = ["compressed_kv_cache_amd/csrc/gva_decode_mfma.hip",
 
 
 def kernel_source_hash():
+    """Hash of the decode kernels' code (comments and whitespace ignored), so
+    counter-derived traffic is reported only for the code it was taken on."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
