@@ -40,8 +40,9 @@ gva_status check_cache_shape(const gva_shape& s) {
   return GVA_OK;
 }
 
+// d_r = 0: no positional slice (the K = V variant when M_h = I, d_n = d_h).
 gva_status check_rope_width(int d_r) {
-  if (d_r < 1) return GVA_ERR_SHAPE;
+  if (d_r < 0) return GVA_ERR_SHAPE;
   if (d_r % 2 || d_r > 64) return GVA_ERR_UNSUPPORTED;
   return GVA_OK;
 }
@@ -143,7 +144,10 @@ gva_status decode(const gva_shape* shape, const float* q, float q_scale, const v
   st = make_plan(s, max_seq_len, keys_separate, &plan);
   if (st != GVA_OK) return st;
   if (s.B == 0) return GVA_OK;
-  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out) return GVA_ERR_NULL;
+  // without a positional slice the GVA path reads no key cache
+  const bool need_keys = keys_separate || s.d_r > 0;
+  if (!q || (need_keys && !k_pool) || !v_pool || !block_table || !seq_lens || !out)
+    return GVA_ERR_NULL;
   if (plan.workspace_bytes && !workspace) return GVA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
       (workspace && !aligned16(workspace)))
@@ -200,7 +204,7 @@ gva_status gva_absorb_query(const gva_shape* shape, const float* q_nope, const f
   gva_status st = check_absorb_shape(s, softmax_scale, rope_base);
   if (st != GVA_OK) return st;
   if (s.B == 0) return GVA_OK;
-  if (!q_nope || !q_rope || !M || !pos || !qa) return GVA_ERR_NULL;
+  if (!q_nope || (s.d_r > 0 && !q_rope) || !M || !pos || !qa) return GVA_ERR_NULL;
   return to_status(gva::launch_absorb(s, q_nope, q_rope, M, pos, absorb_scale(s, softmax_scale),
                                       rope_base, qa, static_cast<hipStream_t>(stream)));
 }
@@ -216,7 +220,8 @@ gva_status gva_append_cache(const gva_shape* shape, const float* v_new, const fl
   if (st != GVA_OK) return st;
   if (!(rope_base > 0.f) || !isfinite(rope_base)) return GVA_ERR_SHAPE;
   if (s.B == 0) return GVA_OK;
-  if (!v_new || !k_new || !pos || !block_table || !v_pool || !k_pool) return GVA_ERR_NULL;
+  if (!v_new || (s.d_r > 0 && (!k_new || !k_pool)) || !pos || !block_table || !v_pool)
+    return GVA_ERR_NULL;
   return to_status(gva::launch_append(s, v_new, k_new, pos, block_table, rope_base, v_pool,
                                       k_pool, static_cast<hipStream_t>(stream)));
 }
@@ -260,10 +265,12 @@ gva_status gva_decode_step(const gva_shape* shape, const float* q_nope, const fl
   st = make_plan(s, max_seq_len, false, &plan);
   if (st != GVA_OK) return st;
   if (s.B == 0) return GVA_OK;
-  if (!q_nope || !q_rope || !M || !v_pool || !k_pool || !block_table || !seq_lens || !out ||
-      !workspace)
+  if (!q_nope || (s.d_r > 0 && (!q_rope || !k_pool)) || !M || !v_pool || !block_table ||
+      !seq_lens || !out || !workspace)
     return GVA_ERR_NULL;
-  if ((v_new == nullptr) != (k_new == nullptr)) return GVA_ERR_NULL;
+  // append requested by v_new; its key part only when there is a positional slice
+  if ((v_new == nullptr && k_new != nullptr) || (v_new && s.d_r > 0 && !k_new))
+    return GVA_ERR_NULL;
   if (!aligned16(v_pool) || !aligned16(k_pool) || !aligned16(out) || !aligned16(workspace))
     return GVA_ERR_ALIGN;
   const size_t qa_off = step_qa_offset(plan.workspace_bytes);

@@ -732,9 +732,11 @@ launch_fn pick(const gva_shape& s, bool gqa) {
     if (s.d_h == 128) return launch_one<4, 128, 0, true>;
     return nullptr;
   }
+  if (s.d_h == 64 && s.d_r == 0) return launch_one<4, 64, 0, false>;
   if (s.d_h == 64 && s.d_r == 16) return launch_one<4, 64, 16, false>;
   if (s.d_h == 64 && s.d_r == 24) return launch_one<4, 64, 24, false>;
   if (s.d_h == 64 && s.d_r == 32) return launch_one<4, 64, 32, false>;
+  if (s.d_h == 128 && s.d_r == 0) return launch_one<4, 128, 0, false>;
   if (s.d_h == 128 && s.d_r == 16) return launch_one<4, 128, 16, false>;
   if (s.d_h == 128 && s.d_r == 32) return launch_one<4, 128, 32, false>;
   return nullptr;

@@ -75,13 +75,20 @@ __device__ __forceinline__ void absorb_block(const PrologueArgs& a, const RopeTa
   const int dq = a.d_h + a.d_r;
 
   // position-slice inputs of this lane's first pair, loaded with the rest
+  // (no positional slice when d_r = 0)
   const int npairs = 16 * half;
+  const int hd = max(half, 1);
   int pi = et * 64 + lane;
-  int p_seq = min(pi / half, 15), p_i = pi % half;
+  int p_seq = min(pi / hd, 15), p_i = pi % hd;
   int p_b = min(b0 + p_seq, a.B - 1);
-  const float* xr = a.q_rope + (static_cast<size_t>(p_b) * a.H + h) * a.d_r + 2 * p_i;
-  float x0 = xr[0], x1 = xr[1];
-  int p_pos = a.pos[p_b] + a.pos_offset;
+  float x0 = 0.f, x1 = 0.f;
+  int p_pos = 0;
+  if (half > 0) {  // uniform
+    const float* xr = a.q_rope + (static_cast<size_t>(p_b) * a.H + h) * a.d_r + 2 * p_i;
+    x0 = xr[0];
+    x1 = xr[1];
+    p_pos = a.pos[p_b] + a.pos_offset;
+  }
 
   const int bq = min(b0 + li, a.B - 1);
   const float* qrow = a.q_nope + (static_cast<size_t>(bq) * a.H + h) * a.d_n;
@@ -137,7 +144,7 @@ __device__ __forceinline__ void absorb_block(const PrologueArgs& a, const RopeTa
   }
 
   const double sc = static_cast<double>(a.scale);
-  for (;;) {
+  while (half > 0) {
     if (pi < npairs && b0 + p_seq < a.B) {
       double y0, y1;
       rotate_f64(x0, x1, p_pos, rt.theta[p_i], &y0, &y1);
@@ -150,7 +157,7 @@ __device__ __forceinline__ void absorb_block(const PrologueArgs& a, const RopeTa
     p_seq = pi / half;
     p_i = pi % half;
     p_b = min(b0 + p_seq, a.B - 1);
-    xr = a.q_rope + (static_cast<size_t>(p_b) * a.H + h) * a.d_r + 2 * p_i;
+    const float* xr = a.q_rope + (static_cast<size_t>(p_b) * a.H + h) * a.d_r + 2 * p_i;
     x0 = xr[0];
     x1 = xr[1];
     p_pos = a.pos[p_b] + a.pos_offset;
@@ -227,7 +234,8 @@ hipError_t launch_prologue(const gva_shape& s, const float* q_nope, const float*
                            const float* k_new, const int32_t* block_table, void* v_pool,
                            void* k_pool, const int32_t* pos, int pos_offset, double base,
                            hipStream_t stream) {
-  if (s.d_h % 16 || s.d_r / 2 > kMaxHalfRope || s.d_r < 2) return hipErrorInvalidValue;
+  if (s.d_h % 16 || s.d_r / 2 > kMaxHalfRope || s.d_r < 0 || s.d_r % 2)
+    return hipErrorInvalidValue;
   PrologueArgs a{};
   a.pos_offset = pos_offset;
   a.q_nope = q_nope;

@@ -71,15 +71,18 @@ typedef enum gva_dtype {
 
 /* Sizes of one call.  Fields an entry point does not use are ignored.
  * Supported: 1 <= H/G, H % G == 0; d_h in {32, 64, 128} (GQA: d_h in
- * {32, 64, 128}); 2 <= d_r <= 64 and even; 1 <= d_n <= 256; block_size == 64;
- * num_blocks, max_blocks >= 1. */
+ * {32, 64, 128}); 0 <= d_r <= 64 and even; 1 <= d_n <= 256; block_size == 64;
+ * num_blocks, max_blocks >= 1.  d_r = 0 drops the positional slice: then
+ * q_rope, k_new and k_pool are not read and may be NULL, and with M_h = I,
+ * d_n = d_h it is the variant whose keys are the values themselves
+ * (bisque.today explainer, Figure 3: half the GQA cache). */
 typedef struct gva_shape {
   int32_t B;           /* sequences in the batch                      */
   int32_t H;           /* query heads                                 */
   int32_t G;           /* value groups                                */
   int32_t d_h;         /* value row width = absorbed content width    */
   int32_t d_n;         /* unrotated content slice of each query head  */
-  int32_t d_r;         /* rotated position slice / shared key width   */
+  int32_t d_r;         /* rotated position slice / shared key width (0: none) */
   int32_t block_size;  /* tokens per cache block                      */
   int32_t max_blocks;  /* columns of block_table                      */
   int32_t num_blocks;  /* blocks in each pool                         */

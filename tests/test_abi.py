@@ -78,7 +78,7 @@ def _ws(g, s, max_seq_len=256):
     (dict(G=0), 2),
     (dict(d_h=48), 3),               # unsupported width
     (dict(d_r=15), 3),               # odd position slice
-    (dict(d_r=0), 2),
+    (dict(d_r=-2), 2),
     (dict(d_r=66), 3),
     (dict(max_blocks=0), 2),
     (dict(num_blocks=0), 2),
@@ -87,6 +87,12 @@ def _ws(g, s, max_seq_len=256):
 def test_workspace_query_validates_shape(g, kw, code):
     st, _ = _ws(g, _shape(g, **kw))
     assert st == code
+
+
+def test_no_positional_slice_is_accepted(g):
+    """d_r = 0 (no positional slice) is a supported width."""
+    st, n = _ws(g, _shape(g, d_r=0))
+    assert st == 0 and n > 0
 
 
 def test_workspace_query_bounds(g):

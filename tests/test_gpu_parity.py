@@ -443,3 +443,67 @@ def test_gqa_ragged_edges(g, gpu, H, G, d_h):
                                 h["seq_lens"])
     assert_bf16_parity(cpu(out).double().numpy(), ref)
     np.testing.assert_allclose(cpu(lse).double().numpy(), ref_lse, atol=1e-3)
+
+
+# --------------------------------------------------------- width variants ----
+
+@pytest.mark.parametrize("H,G,d_h,d_n,dtype", [
+    (16, 4, 64, 48, "bfloat16"),     # matrix cores, d_h 64
+    (32, 8, 128, 96, "bfloat16"),    # matrix cores, d_h 128
+    (8, 8, 32, 24, "float32"),       # vector path
+])
+def test_no_positional_slice(g, gpu, H, G, d_h, d_n, dtype):
+    """d_r = 0: scores use the absorbed content slice only; the fused step
+    appends values only."""
+    base = syn.get_config("long_ragged")
+    cfg = syn.with_overrides(base, B=len(EDGE_LENS), H=H, G=G, d_h=d_h, d_n=d_n, d_r=0,
+                             cache_dtype=dtype, len_range=None, T=None, append=True)
+    lens = torch.tensor(EDGE_LENS, dtype=torch.int32)
+    x, h = gen(cfg, gpu, seq_lens=lens, shuffled=True)
+    announce("no positional slice", H, G, d_h, dtype)
+    out, lse = g.decode_step(x["q_nope"], x["q_rope"], x["M"], x["v_pool"], x["k_pool"],
+                             x["block_table"], x["seq_lens"], x["max_seq_len"],
+                             v_new=x["v_new"], k_new=x["k_new"], rope_base=cfg.rope_base)
+    vp, kp = oracle_pools(h, cfg)
+    ref, ref_lse = o.gva_decode_materialized(
+        h["q_nope"], h["q_rope"], h["M"], vp, kp, h["block_table"], h["seq_lens"],
+        base=cfg.rope_base)
+    if dtype == "float32":
+        assert_fp32_parity(cpu(out), ref)
+    else:
+        assert_bf16_parity(cpu(out).double().numpy(), ref)
+    np.testing.assert_allclose(cpu(lse).double().numpy(), ref_lse, atol=1e-3)
+
+
+def test_keys_equal_values_variant(g, gpu):
+    """M_h = I, d_n = d_h, d_r = 0: the keys are the values themselves, so the
+    decode equals textbook attention of q_nope over K = V (bisque.today
+    explainer, Figure 3: the K = V variant, half the GQA cache)."""
+    cfg = syn.with_overrides(syn.get_config("decode_350m"), B=4, T=1500, d_n=64, d_r=0)
+    x, h = gen(cfg, gpu)
+    eye = torch.eye(cfg.d_h, dtype=torch.float32)
+    x["M"] = eye.expand(cfg.H, -1, -1).contiguous().to(gpu)
+    announce("K = V variant")
+    qa, out, lse = run_step(g, x, cfg)
+    q = cpu(x["q_nope"]).double().numpy()
+    scale = 1.0 / math.sqrt(cfg.d_h)
+    for b in range(cfg.B):
+        sub = seq_subpool(x, b)
+        n = int(x["seq_lens_host"][b])
+        V = sub["v_pool"].double().numpy().reshape(-1, cfg.G, cfg.d_h)[:n]
+        for hh in range(cfg.H):
+            Vg = V[:, o.head_group(hh, cfg.H, cfg.G), :]
+            ref = o.softmax_attention(q[b, hh], Vg, Vg, scale)[0]
+            assert_bf16_parity(cpu(out[b, hh]).double().numpy(), ref, what=f"b={b} h={hh}")
+
+
+def test_additive_head_split(g, gpu):
+    """d_n + d_r > d_h (content width not reduced by the position slice)."""
+    cfg = syn.with_overrides(syn.get_config("decode_350m"), B=6, T=2000, d_n=64, d_r=16)
+    x, h = gen(cfg, gpu)
+    announce("additive split")
+    qa, out, lse = run_step(g, x, cfg)
+    ref, _ = o.gva_decode_materialized(
+        h["q_nope"], h["q_rope"], h["M"], h["v_pool"], h["k_pool"], h["block_table"],
+        h["seq_lens"], base=cfg.rope_base)
+    assert_bf16_parity(cpu(out).double().numpy(), ref)
