@@ -191,16 +191,23 @@ struct WaveCtx {
 // a valid address whose registers are never used.  A real 16-token tile
 // never leaves its 64-slot block, so slots past the sequence end are still
 // inside the pool; the compute steps keep them out of the result.
+//
+// The block-table entry of tile k, read at a clamped index (in bounds for
+// any k >= 0).
+__device__ __forceinline__ int tile_block(const int32_t* bt_row, int j_begin, int max_blocks,
+                                          int k) {
+  return bt_row[min((j_begin + kTileTok * k) / kBlock, max_blocks - 1)];
+}
+
 template <int GT, int DH, int DR, bool GQA>
-__device__ __forceinline__ void load_tile(const WaveCtx& w, int k, int n_tiles,
-                                          TileRegs<GT, DH, DR, GQA>& t, int& bad) {
+__device__ __forceinline__ void load_tile_at(const WaveCtx& w, int k, int n_tiles, int blk,
+                                             TileRegs<GT, DH, DR, GQA>& t, int& bad) {
   using C = Cfg<GT, DH, DR, GQA>;
   // branch-free, so the loads stay in the caller's basic block and issue
-  // where the caller put them: the block-table entry is read at a clamped
-  // index, and a tile past the end, or a bad entry, maps to row 0
+  // where the caller put them: a tile past the end, or a bad entry, maps
+  // to row 0
   const bool real = k < n_tiles;  // uniform
   const int j0 = w.j_begin + kTileTok * k;
-  const int blk = w.bt_row[min(j0 / kBlock, w.max_blocks - 1)];
   const bool in_pool = static_cast<unsigned>(blk) < static_cast<unsigned>(w.num_blocks);
   bad |= (real && !in_pool) ? 1 : 0;  // the chunk is reported NaN
   const size_t row0 = (real && in_pool) ? static_cast<size_t>(blk) * kBlock + (j0 % kBlock) : 0;
@@ -233,6 +240,12 @@ __device__ __forceinline__ void load_tile(const WaveCtx& w, int k, int n_tiles,
       t.r[s] = stream_load8(kr + d);
     }
   }
+}
+
+template <int GT, int DH, int DR, bool GQA>
+__device__ __forceinline__ void load_tile(const WaveCtx& w, int k, int n_tiles,
+                                          TileRegs<GT, DH, DR, GQA>& t, int& bad) {
+  load_tile_at(w, k, n_tiles, tile_block(w.bt_row, w.j_begin, w.max_blocks, k), t, bad);
 }
 
 // Scores of one 16-token tile for this lane's head (tokens 4*q4 .. +3 in
@@ -437,34 +450,66 @@ void decode_mfma_kernel(
   constexpr int kThreads = BC::THREADS;
   __shared__ __attribute__((aligned(16))) unsigned char lds_raw[BC::LDS_BYTES];
 
-  const int c = blockIdx.x, b = blockIdx.y;
+  // Workgroups are handed to the chip's eight XCDs (each with its own L2)
+  // in turn, by linear index.  When the grid is a multiple of 8 the (chunk,
+  // sequence) pairs are renumbered so that all chunks of a sequence fall on
+  // one XCD: the merge traffic of a sequence then stays near one L2.  The
+  // result does not depend on the mapping (the merge uses device-scope
+  // accesses); it only changes where the work runs.
+  int c = blockIdx.x, b = blockIdx.y;
+  if ((num_chunks * gridDim.y) % 8 == 0) {
+    const int n8 = num_chunks * gridDim.y / 8;
+    const int lin = blockIdx.x + blockIdx.y * num_chunks;
+    const int p = (lin % 8) * n8 + lin / 8;  // a permutation of 0 .. grid - 1
+    c = p % num_chunks;
+    b = p / num_chunks;
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int q4 = lane >> 4, li = lane & 15;
   const int nht = H / 16;
   const int ht = wave % nht, sub = wave / nht, nsub = NW / nht;
+  const int head = ht * 16 + li;     // B-operand column of this lane
+  constexpr int DQ = GQA ? DH : DH + DR;
+  const int j_begin = c * chunk_tokens;
+  const int32_t* bt_row = block_table + static_cast<size_t>(b) * max_blocks;
+
+  // Reads that do not depend on the sequence length go out before it (all
+  // in bounds for any length): the block-table entries of this wave's
+  // first tiles and its query row.  Their latencies then overlap the
+  // length's instead of following it, and the first tiles' loads can issue
+  // as soon as the length is known.
+  int blk_first[NSET];
+#pragma unroll
+  for (int i = 0; i < NSET; ++i)
+    blk_first[i] = tile_block(bt_row, j_begin, max_blocks, sub + i * nsub);
+  const float* qrow = q + (static_cast<size_t>(b) * H + head) * DQ;
+  float4 qraw[C::KS][2];
+#pragma unroll
+  for (int s = 0; s < C::KS; ++s) {
+    qraw[s][0] = *reinterpret_cast<const float4*>(qrow + 32 * s + 8 * q4);
+    qraw[s][1] = *reinterpret_cast<const float4*>(qrow + 32 * s + 8 * q4 + 4);
+  }
+  float rraw[C::NRR][4];
+#pragma unroll
+  for (int s = 0; s < C::NRR; ++s)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d = 16 * s + 4 * q4 + e;
+      rraw[s][e] = (!GQA && d < DR) ? qrow[DH + d] : 0.f;
+    }
 
   int len = seq_lens[b];
   int bad = (len < 0 || len > max_seq_len || len > max_blocks * kBlock) ? 1 : 0;
   if (bad) len = 0;
-  const int j_begin = c * chunk_tokens;
-  if (j_begin >= len) {  // uniform over the block
-    if (c == 0) {        // empty or invalid sequence: out = 0 / NaN, lse = -inf / NaN
-      const float v = bad ? __builtin_nanf("") : 0.f;
-      for (int i = threadIdx.x; i < H * DH; i += kThreads)
-        out[static_cast<size_t>(b) * H * DH + i] = v;
-      if (lse)
-        for (int i = threadIdx.x; i < H; i += kThreads)
-          lse[static_cast<size_t>(b) * H + i] = bad ? v : -INFINITY;
-    }
-    return;
-  }
+  // A block past its sequence's end runs no step (no tiles) and leaves
+  // after the loop; there is no branch before it, so nothing above can be
+  // moved below it.
+  const bool active = j_begin < len;  // uniform over the block
   const int j_end = min(len, j_begin + chunk_tokens);
-  const int n_tiles = (j_end - j_begin + kTileTok - 1) / kTileTok;
+  const int n_tiles = active ? (j_end - j_begin + kTileTok - 1) / kTileTok : 0;
 
-  const int head = ht * 16 + li;     // B-operand column of this lane
   const int g0 = ht * GT;            // first value group of the head tile
-  constexpr int DQ = GQA ? DH : DH + DR;
 
   WaveCtx w;
   w.vrow = static_cast<size_t>(G) * DH;
@@ -472,7 +517,7 @@ void decode_mfma_kernel(
   w.v_tile = v_pool + static_cast<size_t>(g0) * DH;
   w.k_tile = k_pool + static_cast<size_t>(g0) * DH;
   w.k_base = GQA ? k_pool + static_cast<size_t>(g0) * DH + 8 * q4 : k_pool;
-  w.bt_row = block_table + static_cast<size_t>(b) * max_blocks;
+  w.bt_row = bt_row;
   w.num_blocks = num_blocks;
   w.max_blocks = max_blocks;
   w.j_begin = j_begin;
@@ -489,11 +534,9 @@ void decode_mfma_kernel(
   QOps<GT, DH, DR, GQA> qo;
   {
     const float qsc = q_scale * kLog2e;
-    const float* qrow = q + (static_cast<size_t>(b) * H + head) * DQ;
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
-      const float4 a = *reinterpret_cast<const float4*>(qrow + 32 * s + 8 * q4);
-      const float4 bb = *reinterpret_cast<const float4*>(qrow + 32 * s + 8 * q4 + 4);
+      const float4 a = qraw[s][0], bb = qraw[s][1];
       const float x[8] = {a.x, a.y, a.z, a.w, bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -508,8 +551,7 @@ void decode_mfma_kernel(
       bf16x4 hh, ll;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int d = 16 * s + 4 * q4 + e;
-        const float x = (!GQA && d < DR) ? qsc * qrow[DH + d] : 0.f;
+        const float x = qsc * rraw[s][e];
         const __bf16 h = static_cast<__bf16>(x);
         hh[e] = h;
         ll[e] = static_cast<__bf16>(x - static_cast<float>(h));
@@ -525,28 +567,25 @@ void decode_mfma_kernel(
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) st.acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- main loop: tiles of 16 tokens, two per step.  Each wave starts on
-  // tiles sub, sub + nsub (, sub + 2 nsub) and then takes the next free tile
-  // of its head tile from an LDS counter when a register set frees up, so
-  // waves whose data arrives first take more tiles and all waves of a block
-  // finish together.  A wave's tile indices increase in the order its sets
-  // are loaded, and the sets are consumed in that order, so the first index
-  // at or past n_tiles ends the wave's loop.
+  // ---- main loop: tiles of 16 tokens, two per step ----
   {
     // This wave's tiles are sub, sub + nsub, ... (n_my of them), taken two
-    // per step.  Full rounds of three steps run in a counted loop and the
-    // last one or two steps follow it: a loop with exits in its middle would
-    // re-enter its head through a merged block, and the compiler then waits
-    // there for every load in flight.  Loads of tiles past n_my read pool
-    // row 0 and are never used.
+    // per step.  The steps run in a counted loop (in rounds of three with
+    // three register sets) and the last steps follow it in straight-line
+    // code: a loop with exits in its middle would re-enter its head through
+    // a merged block, and the compiler then waits there for every load in
+    // flight.  With two sets the final step reloads nothing, so no load is
+    // in flight when the wave reaches the merge (with three, peeling the
+    // last round as well runs out of registers).  A load of a tile past
+    // n_my reads pool row 0 and is never used.
     const int n_my = sub < n_tiles ? (n_tiles - sub + nsub - 1) / nsub : 0;
     const int n_steps = (n_my + 1) / 2;
     auto tile = [&](int i) { return sub + i * nsub; };
     if constexpr (NSET == 3) {
       TileRegs<GT, DH, DR, GQA> ta, tb, tc;
-      load_tile(w, tile(0), n_tiles, ta, bad);
-      load_tile(w, tile(1), n_tiles, tb, bad);
-      load_tile(w, tile(2), n_tiles, tc, bad);
+      load_tile_at(w, tile(0), n_tiles, blk_first[0], ta, bad);
+      load_tile_at(w, tile(1), n_tiles, blk_first[1], tb, bad);
+      load_tile_at(w, tile(2), n_tiles, blk_first[NSET - 1], tc, bad);
       int i = 0;
       for (int r = 0; r < n_steps / 3; ++r, i += 6) {
         pair_step(w, qo, st, n_tiles, bad, ta, tb, tile(i), tile(i + 1), tile(i + 3), tile(i + 4));
@@ -564,12 +603,26 @@ void decode_mfma_kernel(
       }
     } else {
       TileRegs<GT, DH, DR, GQA> ta, tb;
-      load_tile(w, tile(0), n_tiles, ta, bad);
-      load_tile(w, tile(1), n_tiles, tb, bad);
-      for (int i = 0; i < 2 * n_steps; i += 2)
+      load_tile_at(w, tile(0), n_tiles, blk_first[0], ta, bad);
+      load_tile_at(w, tile(1), n_tiles, blk_first[1], tb, bad);
+      int i = 0;
+      for (; i < 2 * n_steps - 2; i += 2)
         pair_step(w, qo, st, n_tiles, bad, ta, tb, tile(i), tile(i + 1), tile(i + 2),
                   tile(i + 3));
+      if (n_steps > 0) last_step(w, qo, st, ta, tb, tile(i), tile(i + 1));
     }
+  }
+
+  if (!active) {
+    if (c == 0) {  // empty or invalid sequence: out = 0 / NaN, lse = -inf / NaN
+      const float v = bad ? __builtin_nanf("") : 0.f;
+      for (int i = threadIdx.x; i < H * DH; i += kThreads)
+        out[static_cast<size_t>(b) * H * DH + i] = v;
+      if (lse)
+        for (int i = threadIdx.x; i < H; i += kThreads)
+          lse[static_cast<size_t>(b) * H + i] = bad ? v : -INFINITY;
+    }
+    return;
   }
 
   // ---- merge the waves of each head tile, write one record per head ----
