@@ -467,8 +467,9 @@ void decode_mfma_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int q4 = lane >> 4, li = lane & 15;
-  const int nht = H / 16;
-  const int ht = wave % nht, sub = wave / nht, nsub = NW / nht;
+  const int nht = H / 16;           // head tiles: 1, 2 or 4
+  const int nht_log2 = nht >> 1;
+  const int ht = wave & (nht - 1), sub = wave >> nht_log2, nsub = NW >> nht_log2;
   const int head = ht * 16 + li;     // B-operand column of this lane
   constexpr int DQ = GQA ? DH : DH + DR;
   const int j_begin = c * chunk_tokens;
@@ -645,40 +646,52 @@ void decode_mfma_kernel(
   const float* all = reinterpret_cast<const float*>(lds_raw);
   float* pb = part + (static_cast<size_t>(b) * num_chunks + c) * H * C::REC;
   const float nan = __builtin_nanf("");
-  for (int i = threadIdx.x; i < nht * 16 * (DH / 4); i += kThreads) {
-    const int hh = i / (DH / 4);          // head within the block's H
-    const int d4 = (i % (DH / 4)) * 4;
+  // VW output dims per thread: 2 where that gives every thread of the block
+  // one item (d_h = 64 with 8 waves), else 4
+  constexpr int VW = (16 * DH <= 2 * kThreads) ? 2 : 4;
+  for (int i = threadIdx.x; i < nht * 16 * (DH / VW); i += kThreads) {
+    const int hh = i / (DH / VW);          // head within the block's H
+    const int dv = (i % (DH / VW)) * VW;
     const int t_ht = hh / 16, n = hh % 16;
-    // the waves of head tile t_ht are t_ht, t_ht + nht, ...; all NW records
-    // are read at once and the others weighted out
+    // the waves of head tile t_ht are t_ht, t_ht + nht, ... (nht is 1, 2
+    // or 4); all NW records are read at once and the others weighted out
     float mv[NW], lv[NW];
-    float4 av[NW];
+    float av[NW][VW];
     float m_star = -INFINITY;
     int any_bad = 0;
 #pragma unroll
     for (int wv = 0; wv < NW; ++wv) {
       const float* rr = all + (wv * 16 + n) * C::REC;
-      mv[wv] = (wv % nht == t_ht) ? rr[0] : -INFINITY;
-      lv[wv] = rr[1];
-      any_bad |= __float_as_int(rr[2]);
-      av[wv] = *reinterpret_cast<const float4*>(rr + 4 + d4);
+      const float4 hd = *reinterpret_cast<const float4*>(rr);
+      mv[wv] = ((wv & (nht - 1)) == t_ht) ? hd.x : -INFINITY;
+      lv[wv] = hd.y;
+      any_bad |= __float_as_int(hd.z);
+      if constexpr (VW == 2) {
+        const float2 a2 = *reinterpret_cast<const float2*>(rr + 4 + dv);
+        av[wv][0] = a2.x;
+        av[wv][1] = a2.y;
+      } else {
+        const float4 a4 = *reinterpret_cast<const float4*>(rr + 4 + dv);
+        av[wv][0] = a4.x;
+        av[wv][1] = a4.y;
+        av[wv][2] = a4.z;
+        av[wv][3] = a4.w;
+      }
       m_star = fmaxf(m_star, mv[wv]);
     }
     float L = 0.f;
-    float4 o = {0.f, 0.f, 0.f, 0.f};
+    float o[VW] = {};
 #pragma unroll
     for (int wv = 0; wv < NW; ++wv) {
       const float wt = (mv[wv] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv[wv] - m_star);
       L = fmaf(wt, lv[wv], L);
-      o.x = fmaf(wt, av[wv].x, o.x);
-      o.y = fmaf(wt, av[wv].y, o.y);
-      o.z = fmaf(wt, av[wv].z, o.z);
-      o.w = fmaf(wt, av[wv].w, o.w);
+#pragma unroll
+      for (int e = 0; e < VW; ++e) o[e] = fmaf(wt, av[wv][e], o[e]);
     }
     float* dst = pb + hh * C::REC;
-    store_dev2(dst + 4 + d4, o.x, o.y);
-    store_dev2(dst + 6 + d4, o.z, o.w);
-    if (d4 == 0) store_dev2(dst, m_star, any_bad ? nan : L);
+#pragma unroll
+    for (int e = 0; e < VW; e += 2) store_dev2(dst + 4 + dv + e, o[e], o[e + 1]);
+    if (dv == 0) store_dev2(dst, m_star, any_bad ? nan : L);
   }
 
   // ---- the last block of this sequence merges its chunk records ----
