@@ -5,14 +5,18 @@ is missing; every operation runs in its HIP kernels.
 """
 from . import _lib
 from ._lib import GvaError, GvaShape, LIB_PATH
-from .ops import (BLOCK_SIZE, absorb_query, append_cache, cache_scalars_per_token,
-                  decode_attention, decode_step, decode_step_workspace_bytes,
-                  decode_workspace_bytes, gqa_decode_attention, gqa_decode_workspace_bytes,
-                  make_shape)
+from .ops import (BLOCK_SIZE, absorb_query, absorb_query_multi, append_cache,
+                  append_cache_multi, cache_scalars_per_token, decode_attention,
+                  decode_attention_multi, decode_step, decode_step_multi,
+                  decode_step_workspace_bytes, decode_workspace_bytes,
+                  decode_workspace_bytes_multi, gqa_decode_attention,
+                  gqa_decode_workspace_bytes, make_shape)
 
 lib = _lib.load()
 
 __all__ = ["BLOCK_SIZE", "GvaError", "GvaShape", "LIB_PATH", "absorb_query",
-           "append_cache", "cache_scalars_per_token", "decode_attention", "decode_step",
-           "decode_step_workspace_bytes",
-           "decode_workspace_bytes", "gqa_decode_attention", "gqa_decode_workspace_bytes", "lib", "make_shape"]
+           "absorb_query_multi", "append_cache", "append_cache_multi",
+           "cache_scalars_per_token", "decode_attention", "decode_attention_multi",
+           "decode_step", "decode_step_multi", "decode_step_workspace_bytes",
+           "decode_workspace_bytes", "decode_workspace_bytes_multi",
+           "gqa_decode_attention", "gqa_decode_workspace_bytes", "lib", "make_shape"]

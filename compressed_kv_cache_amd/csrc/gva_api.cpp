@@ -11,7 +11,7 @@ namespace gva {
 size_t decode_ref_smem_bytes(int H, int dq);
 hipError_t launch_decode_ref(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
                              hipStream_t stream);
-bool mfma_decode_supported(const gva_shape& s, bool keys_separate);
+bool mfma_decode_supported(const gva_shape& s, bool keys_separate, int q_len);
 DecodePlan plan_mfma_decode(const gva_shape& s, int max_seq_len, bool keys_separate);
 hipError_t launch_decode_mfma(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
                               hipStream_t stream);
@@ -24,6 +24,7 @@ constexpr int kRefThreads = 256;
 constexpr int kRefAccMax = 32;
 constexpr size_t kRefSmemMax = 64 * 1024;
 constexpr int kTargetBlocks = 1024;  // split-chunk target for the reference kernel
+constexpr int kMaxQueryTokens = 64;  // query tokens per sequence in one call
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -66,8 +67,22 @@ float absorb_scale(const gva_shape& s, float softmax_scale) {
 
 // Fused step workspace: [decode workspace, padded to 256 B][qa].
 size_t step_qa_offset(size_t decode_bytes) { return ((decode_bytes + 255) / 256) * 256; }
-size_t step_qa_bytes(const gva_shape& s) {
-  return static_cast<size_t>(s.B) * s.H * (s.d_h + s.d_r) * sizeof(float);
+size_t step_qa_bytes(const gva_shape& s, int q_len) {
+  return static_cast<size_t>(s.B) * s.H * q_len * (s.d_h + s.d_r) * sizeof(float);
+}
+
+gva_status check_q_len(int32_t q_len) {
+  if (q_len < 1) return GVA_ERR_SHAPE;
+  if (q_len > kMaxQueryTokens) return GVA_ERR_UNSUPPORTED;
+  return GVA_OK;
+}
+
+// The decode kernels see one column per (head, query token): H * q_len
+// heads, H/G * q_len of them per value group.
+gva_shape columns(const gva_shape& s, int q_len) {
+  gva_shape c = s;
+  c.H = s.H * q_len;
+  return c;
 }
 
 int round_up(long long x, int m) { return static_cast<int>(((x + m - 1) / m) * m); }
@@ -93,10 +108,11 @@ gva_status ref_supported(const gva_shape& s, bool keys_separate) {
   return GVA_OK;
 }
 
-// Picks the kernel for a decode call; fails when neither kernel covers it.
-gva_status make_plan(const gva_shape& s, int max_seq_len, bool keys_separate,
+// Picks the kernel for a decode call (s: one column per head and query
+// token); fails when neither kernel covers it.
+gva_status make_plan(const gva_shape& s, int max_seq_len, bool keys_separate, int q_len,
                      gva::DecodePlan* plan) {
-  if (gva::mfma_decode_supported(s, keys_separate)) {
+  if (gva::mfma_decode_supported(s, keys_separate, q_len)) {
     *plan = gva::plan_mfma_decode(s, max_seq_len, keys_separate);
     return GVA_OK;
   }
@@ -106,9 +122,12 @@ gva_status make_plan(const gva_shape& s, int max_seq_len, bool keys_separate,
   return GVA_OK;
 }
 
-gva_status check_decode_args(const gva_shape* shape, int32_t max_seq_len, bool keys_separate) {
+gva_status check_decode_args(const gva_shape* shape, int32_t max_seq_len, bool keys_separate,
+                             int32_t q_len) {
   if (!shape) return GVA_ERR_NULL;
   gva_status st = check_cache_shape(*shape);
+  if (st != GVA_OK) return st;
+  st = check_q_len(q_len);
   if (st != GVA_OK) return st;
   if (!keys_separate) {
     st = check_rope_width(shape->d_r);
@@ -122,26 +141,27 @@ gva_status check_decode_args(const gva_shape* shape, int32_t max_seq_len, bool k
 }
 
 gva_status workspace_size(const gva_shape* shape, int32_t max_seq_len, bool keys_separate,
-                          size_t* bytes) {
+                          int32_t q_len, size_t* bytes) {
   if (!bytes) return GVA_ERR_NULL;
-  gva_status st = check_decode_args(shape, max_seq_len, keys_separate);
+  gva_status st = check_decode_args(shape, max_seq_len, keys_separate, q_len);
   if (st != GVA_OK) return st;
   gva::DecodePlan plan;
-  st = make_plan(*shape, max_seq_len, keys_separate, &plan);
+  st = make_plan(columns(*shape, q_len), max_seq_len, keys_separate, q_len, &plan);
   if (st != GVA_OK) return st;
   *bytes = plan.workspace_bytes;
   return GVA_OK;
 }
 
-gva_status decode(const gva_shape* shape, const float* q, float q_scale, const void* k_pool,
-                  const void* v_pool, const int32_t* block_table, const int32_t* seq_lens,
-                  int32_t max_seq_len, void* workspace, size_t workspace_bytes, float* out,
-                  float* lse, void* stream, bool keys_separate) {
-  gva_status st = check_decode_args(shape, max_seq_len, keys_separate);
+gva_status decode(const gva_shape* shape, int32_t q_len, const float* q, float q_scale,
+                  const void* k_pool, const void* v_pool, const int32_t* block_table,
+                  const int32_t* seq_lens, int32_t max_seq_len, void* workspace,
+                  size_t workspace_bytes, float* out, float* lse, void* stream,
+                  bool keys_separate) {
+  gva_status st = check_decode_args(shape, max_seq_len, keys_separate, q_len);
   if (st != GVA_OK) return st;
-  const gva_shape& s = *shape;
+  const gva_shape s = columns(*shape, q_len);
   gva::DecodePlan plan;
-  st = make_plan(s, max_seq_len, keys_separate, &plan);
+  st = make_plan(s, max_seq_len, keys_separate, q_len, &plan);
   if (st != GVA_OK) return st;
   if (s.B == 0) return GVA_OK;
   // without a positional slice the GVA path reads no key cache
@@ -165,6 +185,7 @@ gva_status decode(const gva_shape* shape, const float* q, float q_scale, const v
   a.out = out;
   a.lse = lse;
   a.q_scale = q_scale;
+  a.q_len = q_len;
   a.keys_separate = keys_separate;
   hipStream_t strm = static_cast<hipStream_t>(stream);
   if (plan.kernel == gva::kKernelMfma) return to_status(gva::launch_decode_mfma(s, plan, a, strm));
@@ -196,73 +217,116 @@ uint64_t gva_cache_scalars_per_token(const gva_shape* shape) {
          static_cast<uint64_t>(shape->d_r);
 }
 
-gva_status gva_absorb_query(const gva_shape* shape, const float* q_nope, const float* q_rope,
-                            const float* M, const int32_t* pos, float softmax_scale,
-                            float rope_base, float* qa, void* stream) {
+gva_status gva_absorb_query_multi(const gva_shape* shape, int32_t q_len, const float* q_nope,
+                                  const float* q_rope, const float* M, const int32_t* pos,
+                                  float softmax_scale, float rope_base, float* qa,
+                                  void* stream) {
   if (!shape) return GVA_ERR_NULL;
   const gva_shape& s = *shape;
   gva_status st = check_absorb_shape(s, softmax_scale, rope_base);
   if (st != GVA_OK) return st;
+  st = check_q_len(q_len);
+  if (st != GVA_OK) return st;
   if (s.B == 0) return GVA_OK;
   if (!q_nope || (s.d_r > 0 && !q_rope) || !M || !pos || !qa) return GVA_ERR_NULL;
-  return to_status(gva::launch_absorb(s, q_nope, q_rope, M, pos, absorb_scale(s, softmax_scale),
-                                      rope_base, qa, static_cast<hipStream_t>(stream)));
+  return to_status(gva::launch_absorb(s, q_len, q_nope, q_rope, M, pos,
+                                      absorb_scale(s, softmax_scale), rope_base, qa,
+                                      static_cast<hipStream_t>(stream)));
 }
 
-gva_status gva_append_cache(const gva_shape* shape, const float* v_new, const float* k_new,
-                            const int32_t* pos, const int32_t* block_table, float rope_base,
-                            void* v_pool, void* k_pool, void* stream) {
+gva_status gva_absorb_query(const gva_shape* shape, const float* q_nope, const float* q_rope,
+                            const float* M, const int32_t* pos, float softmax_scale,
+                            float rope_base, float* qa, void* stream) {
+  return gva_absorb_query_multi(shape, 1, q_nope, q_rope, M, pos, softmax_scale, rope_base, qa,
+                                stream);
+}
+
+gva_status gva_append_cache_multi(const gva_shape* shape, int32_t q_len, const float* v_new,
+                                  const float* k_new, const int32_t* pos,
+                                  const int32_t* block_table, float rope_base, void* v_pool,
+                                  void* k_pool, void* stream) {
   if (!shape) return GVA_ERR_NULL;
   const gva_shape& s = *shape;
   gva_status st = check_cache_shape(s);
   if (st != GVA_OK) return st;
   st = check_rope_width(s.d_r);
   if (st != GVA_OK) return st;
+  st = check_q_len(q_len);
+  if (st != GVA_OK) return st;
   if (!(rope_base > 0.f) || !isfinite(rope_base)) return GVA_ERR_SHAPE;
   if (s.B == 0) return GVA_OK;
   if (!v_new || (s.d_r > 0 && (!k_new || !k_pool)) || !pos || !block_table || !v_pool)
     return GVA_ERR_NULL;
-  return to_status(gva::launch_append(s, v_new, k_new, pos, block_table, rope_base, v_pool,
-                                      k_pool, static_cast<hipStream_t>(stream)));
+  return to_status(gva::launch_append(s, q_len, v_new, k_new, pos, block_table, rope_base,
+                                      v_pool, k_pool, static_cast<hipStream_t>(stream)));
+}
+
+gva_status gva_append_cache(const gva_shape* shape, const float* v_new, const float* k_new,
+                            const int32_t* pos, const int32_t* block_table, float rope_base,
+                            void* v_pool, void* k_pool, void* stream) {
+  return gva_append_cache_multi(shape, 1, v_new, k_new, pos, block_table, rope_base, v_pool,
+                                k_pool, stream);
+}
+
+gva_status gva_decode_workspace_size_multi(const gva_shape* shape, int32_t q_len,
+                                           int32_t max_seq_len, size_t* bytes) {
+  return workspace_size(shape, max_seq_len, false, q_len, bytes);
 }
 
 gva_status gva_decode_workspace_size(const gva_shape* shape, int32_t max_seq_len,
                                      size_t* bytes) {
-  return workspace_size(shape, max_seq_len, false, bytes);
+  return workspace_size(shape, max_seq_len, false, 1, bytes);
+}
+
+gva_status gva_decode_attention_multi(const gva_shape* shape, int32_t q_len, const float* qa,
+                                      const void* v_pool, const void* k_pool,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      int32_t max_seq_len, void* workspace,
+                                      size_t workspace_bytes, float* out, float* lse,
+                                      void* stream) {
+  return decode(shape, q_len, qa, 1.0f, k_pool, v_pool, block_table, seq_lens, max_seq_len,
+                workspace, workspace_bytes, out, lse, stream, false);
 }
 
 gva_status gva_decode_attention(const gva_shape* shape, const float* qa, const void* v_pool,
                                 const void* k_pool, const int32_t* block_table,
                                 const int32_t* seq_lens, int32_t max_seq_len, void* workspace,
                                 size_t workspace_bytes, float* out, float* lse, void* stream) {
-  return decode(shape, qa, 1.0f, k_pool, v_pool, block_table, seq_lens, max_seq_len, workspace,
-                workspace_bytes, out, lse, stream, false);
+  return decode(shape, 1, qa, 1.0f, k_pool, v_pool, block_table, seq_lens, max_seq_len,
+                workspace, workspace_bytes, out, lse, stream, false);
+}
+
+gva_status gva_decode_step_workspace_size_multi(const gva_shape* shape, int32_t q_len,
+                                                int32_t max_seq_len, size_t* bytes) {
+  if (!bytes) return GVA_ERR_NULL;
+  size_t dec = 0;
+  gva_status st = workspace_size(shape, max_seq_len, false, q_len, &dec);
+  if (st != GVA_OK) return st;
+  *bytes = step_qa_offset(dec) + step_qa_bytes(*shape, q_len);
+  return GVA_OK;
 }
 
 gva_status gva_decode_step_workspace_size(const gva_shape* shape, int32_t max_seq_len,
                                           size_t* bytes) {
-  if (!bytes) return GVA_ERR_NULL;
-  size_t dec = 0;
-  gva_status st = workspace_size(shape, max_seq_len, false, &dec);
-  if (st != GVA_OK) return st;
-  *bytes = step_qa_offset(dec) + step_qa_bytes(*shape);
-  return GVA_OK;
+  return gva_decode_step_workspace_size_multi(shape, 1, max_seq_len, bytes);
 }
 
-gva_status gva_decode_step(const gva_shape* shape, const float* q_nope, const float* q_rope,
-                           const float* M, float softmax_scale, float rope_base,
-                           const float* v_new, const float* k_new, void* v_pool, void* k_pool,
-                           const int32_t* block_table, const int32_t* seq_lens,
-                           int32_t max_seq_len, void* workspace, size_t workspace_bytes,
-                           float* out, float* lse, void* stream) {
+gva_status gva_decode_step_multi(const gva_shape* shape, int32_t q_len, const float* q_nope,
+                                 const float* q_rope, const float* M, float softmax_scale,
+                                 float rope_base, const float* v_new, const float* k_new,
+                                 void* v_pool, void* k_pool, const int32_t* block_table,
+                                 const int32_t* seq_lens, int32_t max_seq_len, void* workspace,
+                                 size_t workspace_bytes, float* out, float* lse,
+                                 void* stream) {
   if (!shape) return GVA_ERR_NULL;
   const gva_shape& s = *shape;
   gva_status st = check_absorb_shape(s, softmax_scale, rope_base);
   if (st != GVA_OK) return st;
-  st = check_decode_args(shape, max_seq_len, false);
+  st = check_decode_args(shape, max_seq_len, false, q_len);
   if (st != GVA_OK) return st;
   gva::DecodePlan plan;
-  st = make_plan(s, max_seq_len, false, &plan);
+  const gva_shape sc = columns(s, q_len);
+  st = make_plan(sc, max_seq_len, false, q_len, &plan);
   if (st != GVA_OK) return st;
   if (s.B == 0) return GVA_OK;
   if (!q_nope || (s.d_r > 0 && (!q_rope || !k_pool)) || !M || !v_pool || !block_table ||
@@ -274,13 +338,14 @@ gva_status gva_decode_step(const gva_shape* shape, const float* q_nope, const fl
   if (!aligned16(v_pool) || !aligned16(k_pool) || !aligned16(out) || !aligned16(workspace))
     return GVA_ERR_ALIGN;
   const size_t qa_off = step_qa_offset(plan.workspace_bytes);
-  if (workspace_bytes < qa_off + step_qa_bytes(s)) return GVA_ERR_WORKSPACE;
+  if (workspace_bytes < qa_off + step_qa_bytes(s, q_len)) return GVA_ERR_WORKSPACE;
   float* qa = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + qa_off);
   hipStream_t strm = static_cast<hipStream_t>(stream);
-  // append (optional) + absorb in one launch; query position = seq_lens[b] - 1
+  // append (optional) + absorb in one launch; the last new token and the
+  // last query sit at position seq_lens[b] - 1
   hipError_t e = gva::launch_prologue(s, q_nope, q_rope, M, absorb_scale(s, softmax_scale), qa,
                                       v_new, k_new, block_table, v_pool, k_pool, seq_lens, -1,
-                                      rope_base, strm);
+                                      q_len, rope_base, strm);
   if (e != hipSuccess) return GVA_ERR_HIP;
   gva::DecodeArgs a{};
   a.q = qa;
@@ -294,14 +359,26 @@ gva_status gva_decode_step(const gva_shape* shape, const float* q_nope, const fl
   a.out = out;
   a.lse = lse;
   a.q_scale = 1.0f;
+  a.q_len = q_len;
   a.keys_separate = false;
-  if (plan.kernel == gva::kKernelMfma) return to_status(gva::launch_decode_mfma(s, plan, a, strm));
-  return to_status(gva::launch_decode_ref(s, plan, a, strm));
+  if (plan.kernel == gva::kKernelMfma) return to_status(gva::launch_decode_mfma(sc, plan, a, strm));
+  return to_status(gva::launch_decode_ref(sc, plan, a, strm));
+}
+
+gva_status gva_decode_step(const gva_shape* shape, const float* q_nope, const float* q_rope,
+                           const float* M, float softmax_scale, float rope_base,
+                           const float* v_new, const float* k_new, void* v_pool, void* k_pool,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                           float* out, float* lse, void* stream) {
+  return gva_decode_step_multi(shape, 1, q_nope, q_rope, M, softmax_scale, rope_base, v_new,
+                               k_new, v_pool, k_pool, block_table, seq_lens, max_seq_len,
+                               workspace, workspace_bytes, out, lse, stream);
 }
 
 gva_status gqa_decode_workspace_size(const gva_shape* shape, int32_t max_seq_len,
                                      size_t* bytes) {
-  return workspace_size(shape, max_seq_len, true, bytes);
+  return workspace_size(shape, max_seq_len, true, 1, bytes);
 }
 
 gva_status gqa_decode_attention(const gva_shape* shape, const float* q, float softmax_scale,
@@ -313,8 +390,8 @@ gva_status gqa_decode_attention(const gva_shape* shape, const float* q, float so
   float scale = softmax_scale;
   if (shape && !(scale > 0.f) && shape->d_h > 0)
     scale = 1.0f / sqrtf(static_cast<float>(shape->d_h));
-  return decode(shape, q, scale, k_pool, v_pool, block_table, seq_lens, max_seq_len, workspace,
-                workspace_bytes, out, lse, stream, true);
+  return decode(shape, 1, q, scale, k_pool, v_pool, block_table, seq_lens, max_seq_len,
+                workspace, workspace_bytes, out, lse, stream, true);
 }
 
 }  // extern "C"

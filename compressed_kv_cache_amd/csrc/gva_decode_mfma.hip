@@ -81,7 +81,9 @@ __device__ __forceinline__ int swz(int row) {
   return ((i << 1) | (i >> 3)) & 15;
 }
 __device__ __forceinline__ int lds_off(int row, int chunk, int ROWB) {
-  return row * ROWB + ((chunk ^ swz(row)) << 4);
+  // rows of 8 chunks (one 64-wide group) permute within the row
+  const int sw = ROWB >= 256 ? swz(row) : (swz(row) & (ROWB / 16 - 1));
+  return row * ROWB + ((chunk ^ sw) << 4);
 }
 
 // GVA tiles are read in 1 KB pieces: piece x of a wave covers bytes
@@ -180,6 +182,7 @@ struct WaveCtx {
   const int32_t* bt_row;   // block_table row of this sequence
   size_t vrow;             // elements per value (or key) row
   int num_blocks, max_blocks, j_begin, j_end, q4, li, lg;
+  int j_end_q;             // this lane's query sees tokens < j_end_q (causal)
   int lrow, lchunk;        // GVA pieces: this lane's row and chunk in piece 0
   unsigned loff;           // ... and its byte offset from the piece's base
   unsigned char* lds;      // this wave's LDS tile (2 x 16 rows)
@@ -355,15 +358,20 @@ __device__ __forceinline__ void softmax_pv(const WaveCtx& w, int cntA, int cntB,
   const bool raise = tmax > st.m + kLazy;
   if (__any(raise)) {  // uniform: rare after the first pair
     const float m_new = raise ? tmax : st.m;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    // lanes that keep their max keep their sums (also when the max is
+    // still -inf, where exp2(m - m_new) would be NaN)
+    const float alpha = raise ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
     st.l *= alpha;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) st.acc[dt] *= alpha;
     st.m = m_new;
   }
+  // with several query tokens a lane may have seen no token yet (max still
+  // -inf): its weights are then exp2(-inf) = 0, not exp2(-inf + inf)
+  const float mref = (GT < 4 && st.m == -INFINITY) ? 0.f : st.m;
   float p[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sv[j] - st.m);
+  for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sv[j] - mref);
   st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   bf16x8 ph, pl;
 #pragma unroll
@@ -397,6 +405,12 @@ __device__ __forceinline__ void softmax_pv(const WaveCtx& w, int cntA, int cntB,
   wave_lds_fence();
 }
 
+// Tokens of tile k this lane's query sees (the tile's token count, less the
+// positions past the query with several query tokens).
+__device__ __forceinline__ int lane_count(const WaveCtx& w, int k) {
+  return max(0, min(kTileTok, w.j_end_q - (w.j_begin + kTileTok * k)));
+}
+
 // Tile-pair step on the sets (x, y) holding tiles kx < ky: the scores and
 // LDS staging of each tile, each set reloaded with its next tile (nx, ny;
 // y only if RELOAD_Y) as soon as its scores are taken, then the softmax and
@@ -418,7 +432,7 @@ __device__ __forceinline__ void pair_step(const WaveCtx& w, const QOps<GT, DH, D
   __builtin_amdgcn_sched_barrier(0);
   const f32x4 sb = score_and_stage(w, cy, y, qo, 1);
   if constexpr (RELOAD_Y) load_tile(w, ny, n_tiles, y, bad);
-  softmax_pv(w, cx, cy, sa, sb, st);
+  softmax_pv(w, lane_count(w, kx), lane_count(w, ky), sa, sb, st);
 }
 
 // The final step: no reloads.
@@ -431,7 +445,7 @@ __device__ __forceinline__ void last_step(const WaveCtx& w, const QOps<GT, DH, D
   const int cy = max(0, min(kTileTok, w.j_end - (w.j_begin + kTileTok * ky)));
   const f32x4 sa = score_and_stage(w, cx, x, qo, 0);
   const f32x4 sb = score_and_stage(w, cy, y, qo, 1);
-  softmax_pv(w, cx, cy, sa, sb, st);
+  softmax_pv(w, lane_count(w, kx), lane_count(w, ky), sa, sb, st);
 }
 
 // NW: waves per block.  WPE: waves per SIMD the register budget is sized
@@ -443,7 +457,8 @@ void decode_mfma_kernel(
     const float* __restrict__ q, const bf16_t* __restrict__ v_pool,
     const bf16_t* __restrict__ k_pool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int max_seq_len, int H, int G, int max_blocks,
-    int num_blocks, int chunk_tokens, int num_chunks, float q_scale, float* __restrict__ part,
+    int num_blocks, int chunk_tokens, int num_chunks, int q_len, float q_scale,
+    float* __restrict__ part,
     unsigned* __restrict__ tickets, float* __restrict__ out, float* __restrict__ lse) {
   using C = Cfg<GT, DH, DR, GQA>;
   using BC = BlockCfg<C, NW>;
@@ -467,8 +482,8 @@ void decode_mfma_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int q4 = lane >> 4, li = lane & 15;
-  const int nht = H / 16;           // head tiles: 1, 2 or 4
-  const int nht_log2 = nht >> 1;
+  const int nht = H / 16;           // head tiles: a power of two <= NW
+  const int nht_log2 = __builtin_ctz(nht);
   const int ht = wave & (nht - 1), sub = wave >> nht_log2, nsub = NW >> nht_log2;
   const int head = ht * 16 + li;     // B-operand column of this lane
   constexpr int DQ = GQA ? DH : DH + DR;
@@ -501,7 +516,8 @@ void decode_mfma_kernel(
     }
 
   int len = seq_lens[b];
-  int bad = (len < 0 || len > max_seq_len || len > max_blocks * kBlock) ? 1 : 0;
+  int bad = (len < 0 || len > max_seq_len || len > max_blocks * kBlock ||
+             (len > 0 && len < q_len)) ? 1 : 0;
   if (bad) len = 0;
   // A block past its sequence's end runs no step (no tiles) and leaves
   // after the loop; there is no branch before it, so nothing above can be
@@ -523,6 +539,8 @@ void decode_mfma_kernel(
   w.max_blocks = max_blocks;
   w.j_begin = j_begin;
   w.j_end = j_end;
+  // query token i of L (head = h * L + i) sits at position len - L + i
+  w.j_end_q = min(j_end, len - (q_len - 1 - head % q_len));
   w.q4 = q4;
   w.li = li;
   w.lg = li / (16 / GT);
@@ -771,40 +789,54 @@ hipError_t launch_one(const gva_shape& s, const DecodePlan& plan, const DecodeAr
   // 4 waves per block.
   constexpr int NW = (DH == 64 && !GQA) ? 8 : 4;
   constexpr int WPE = (DH == 64 && !GQA) ? 2 : 1;
-  constexpr int NSET = GQA && DH == 64 ? 3 : 2;
+  // three register sets where tiles are narrow (GQA d_h = 64, and one or
+  // two value groups per head tile, where each tile is only 2-4 KB)
+  constexpr int NSET = (GQA && DH == 64) || GT < 4 ? 3 : 2;
   if ((s.H / 16) > NW || NW % (s.H / 16) != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL((decode_mfma_kernel<GT, DH, DR, GQA, NW, WPE, NSET>), grid, dim3(64 * NW),
                      0, stream,
                      a.q, static_cast<const bf16_t*>(a.v_pool),
                      static_cast<const bf16_t*>(a.k_pool), a.block_table, a.seq_lens,
                      a.max_seq_len, s.H, s.G, s.max_blocks, s.num_blocks, plan.chunk_tokens,
-                     plan.num_chunks, a.q_scale, a.partials, a.tickets, a.out, a.lse);
+                     plan.num_chunks, a.q_len, a.q_scale, a.partials, a.tickets, a.out, a.lse);
   return hipGetLastError();
 }
 
 typedef hipError_t (*launch_fn)(const gva_shape&, const DecodePlan&, const DecodeArgs&,
                                 hipStream_t);
 
-// Instantiated widths: (groups per head tile, d_h, d_r).
-launch_fn pick(const gva_shape& s, bool gqa) {
+template <int GT>
+launch_fn pick_width(int d_h, int d_r) {
+  if (d_h == 64 && d_r == 0) return launch_one<GT, 64, 0, false>;
+  if (d_h == 64 && d_r == 16) return launch_one<GT, 64, 16, false>;
+  if (d_h == 64 && d_r == 24) return launch_one<GT, 64, 24, false>;
+  if (d_h == 64 && d_r == 32) return launch_one<GT, 64, 32, false>;
+  if (d_h == 128 && d_r == 0) return launch_one<GT, 128, 0, false>;
+  if (d_h == 128 && d_r == 16) return launch_one<GT, 128, 16, false>;
+  if (d_h == 128 && d_r == 32) return launch_one<GT, 128, 32, false>;
+  return nullptr;
+}
+
+// Instantiated widths: (groups per head tile, d_h, d_r).  s.H counts query
+// heads times query tokens (head h, token i -> column h * L + i), so a head
+// tile of 16 columns covers 16 / (columns per group) groups: 4 for one query
+// token at H/G = 4, 2 or 1 for two or four query tokens (or H/G = 8, 16).
+launch_fn pick(const gva_shape& s, bool gqa, int q_len) {
   // head tiles of 16 must divide the waves of a block (4 or 8)
   if (s.cache_dtype != GVA_BF16 || s.H % 16 != 0) return nullptr;
   const int nht = s.H / 16;
-  if (nht != 1 && nht != 2 && nht != 4) return nullptr;
-  const int hpg = s.H / s.G;
-  if (hpg != 4) return nullptr;
+  if (nht & (nht - 1)) return nullptr;
+  if (nht > (s.d_h == 64 && !gqa ? 8 : 4)) return nullptr;
+  const int hpg = s.H / s.G;  // columns per group
   if (gqa) {
+    if (hpg != 4 || q_len != 1) return nullptr;
     if (s.d_h == 64) return launch_one<4, 64, 0, true>;
     if (s.d_h == 128) return launch_one<4, 128, 0, true>;
     return nullptr;
   }
-  if (s.d_h == 64 && s.d_r == 0) return launch_one<4, 64, 0, false>;
-  if (s.d_h == 64 && s.d_r == 16) return launch_one<4, 64, 16, false>;
-  if (s.d_h == 64 && s.d_r == 24) return launch_one<4, 64, 24, false>;
-  if (s.d_h == 64 && s.d_r == 32) return launch_one<4, 64, 32, false>;
-  if (s.d_h == 128 && s.d_r == 0) return launch_one<4, 128, 0, false>;
-  if (s.d_h == 128 && s.d_r == 16) return launch_one<4, 128, 16, false>;
-  if (s.d_h == 128 && s.d_r == 32) return launch_one<4, 128, 32, false>;
+  if (hpg == 4 && q_len == 1) return pick_width<4>(s.d_h, s.d_r);
+  if (hpg == 8) return pick_width<2>(s.d_h, s.d_r);
+  if (hpg == 16) return pick_width<1>(s.d_h, s.d_r);
   return nullptr;
 }
 
@@ -815,9 +847,9 @@ int env_int(const char* name, int dflt) {
 
 }  // namespace
 
-bool mfma_decode_supported(const gva_shape& s, bool keys_separate) {
+bool mfma_decode_supported(const gva_shape& s, bool keys_separate, int q_len) {
   if (env_int("GVA_FORCE_REF", 0)) return false;
-  return pick(s, keys_separate) != nullptr;
+  return pick(s, keys_separate, q_len) != nullptr;
 }
 
 // Chunking: enough blocks to keep every CU streaming (target ~1-2 per CU
@@ -843,7 +875,7 @@ DecodePlan plan_mfma_decode(const gva_shape& s, int max_seq_len, bool keys_separ
 
 hipError_t launch_decode_mfma(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
                               hipStream_t stream) {
-  launch_fn f = pick(s, a.keys_separate);
+  launch_fn f = pick(s, a.keys_separate, a.q_len);
   if (!f) return hipErrorInvalidValue;
   return f(s, plan, a, stream);
 }

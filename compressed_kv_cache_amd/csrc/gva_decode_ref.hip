@@ -3,7 +3,8 @@
 // general fallback; bf16 caches at the tuned widths take the MFMA kernel.
 //
 // Work split: block (c, b) scans chunk c of sequence b one 64-token cache
-// block at a time, keeping a running (max, sum, accumulator) softmax state
+// block at a time (H counts query heads times query tokens: column h*L + i is
+// query token i of head h, at position len - L + i, masked causally), keeping a running (max, sum, accumulator) softmax state
 // per head; the merge kernel combines the chunks by log-sum-exp.  Scores are
 // kept in log2 units (query pre-multiplied by log2 e) so exp2 is used.
 #include "gva_device.h"
@@ -24,7 +25,7 @@ __global__ __launch_bounds__(kThreads) void decode_ref_kernel(
     const float* __restrict__ q, const CT* __restrict__ v_pool, const CT* __restrict__ k_pool,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     int max_seq_len, int H, int G, int d_h, int d_r, int max_blocks, int num_blocks,
-    int chunk_tokens, int num_chunks, float q_scale, float* __restrict__ part) {
+    int chunk_tokens, int num_chunks, int q_len, float q_scale, float* __restrict__ part) {
   extern __shared__ float smem[];
   const int dq = KS ? d_h : d_h + d_r;
   float* q_s = smem;                 // [H][dq], log2-scaled
@@ -38,7 +39,8 @@ __global__ __launch_bounds__(kThreads) void decode_ref_kernel(
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int hpg = H / G;
   int len = seq_lens[b];
-  const bool bad_len = len < 0 || len > max_seq_len || len > max_blocks * kTile;
+  const bool bad_len = len < 0 || len > max_seq_len || len > max_blocks * kTile ||
+                       (len > 0 && len < q_len);
   if (bad_len) len = 0;
   const int j_begin = c * chunk_tokens;
   if (j_begin >= len) return;  // empty chunk (bad lengths are flagged by the merge)
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void decode_ref_kernel(
     for (int i = t; i < H * kTile; i += kThreads) {
       const int h = i / kTile, jj = i % kTile;
       float s = -INFINITY;
-      if (jj < cnt) {
+      if (jj < cnt && j0 + jj <= len - q_len + h % q_len) {  // causal over query tokens
         const int g = h / hpg;
         const float* qh = q_s + h * dq;
         const size_t row = base_row + jj;
@@ -153,12 +155,13 @@ constexpr int kMergeMaxChunks = 1024;
 
 __global__ __launch_bounds__(64) void merge_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ seq_lens, int max_seq_len,
-    int max_tokens, int H, int d_h, int chunk_tokens, int num_chunks, float* __restrict__ out,
-    float* __restrict__ lse) {
+    int max_tokens, int H, int d_h, int chunk_tokens, int num_chunks, int q_len,
+    float* __restrict__ out, float* __restrict__ lse) {
   __shared__ float w_s[kMergeMaxChunks];
   const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int len = seq_lens[b];
-  const bool bad_len = len < 0 || len > max_seq_len || len > max_tokens;
+  const bool bad_len = len < 0 || len > max_seq_len || len > max_tokens ||
+                       (len > 0 && len < q_len);
   const int rec = d_h + 4;
   float* ob = out + (static_cast<size_t>(b) * H + h) * d_h;
   const float nan = __builtin_nanf("");
@@ -209,8 +212,8 @@ hipError_t launch_decode_ref(const gva_shape& s, const DecodePlan& plan, const D
   hipLaunchKernelGGL((decode_ref_kernel<CT, KS>), grid, dim3(kThreads), smem, stream, a.q,     \
                      static_cast<const CT*>(a.v_pool), static_cast<const CT*>(a.k_pool),        \
                      a.block_table, a.seq_lens, a.max_seq_len, s.H, s.G, s.d_h, s.d_r,          \
-                     s.max_blocks, s.num_blocks, plan.chunk_tokens, plan.num_chunks, a.q_scale, \
-                     a.partials)
+                     s.max_blocks, s.num_blocks, plan.chunk_tokens, plan.num_chunks, a.q_len,   \
+                     a.q_scale, a.partials)
   if (bf) {
     if (a.keys_separate) GVA_LAUNCH_REF(bf16_t, true); else GVA_LAUNCH_REF(bf16_t, false);
   } else {
@@ -226,7 +229,7 @@ hipError_t launch_merge(const gva_shape& s, const DecodePlan& plan, const Decode
                         hipStream_t stream) {
   hipLaunchKernelGGL(merge_kernel, dim3(s.H, s.B), dim3(64), 0, stream, a.partials, a.seq_lens,
                      a.max_seq_len, s.max_blocks * kTile, s.H, s.d_h, plan.chunk_tokens,
-                     plan.num_chunks, a.out, a.lse);
+                     plan.num_chunks, a.q_len, a.out, a.lse);
   return hipGetLastError();
 }
 

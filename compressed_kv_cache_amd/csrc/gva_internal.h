@@ -32,25 +32,28 @@ enum { kKernelRef = 0, kKernelMfma = 1 };
 DecodePlan plan_gva_decode(const gva_shape& s, int max_seq_len);
 DecodePlan plan_gqa_decode(const gva_shape& s, int max_seq_len);
 
-hipError_t launch_absorb(const gva_shape& s, const float* q_nope, const float* q_rope,
-                         const float* M, const int32_t* pos, float scale, double base,
-                         float* qa, hipStream_t stream);
+// q_len tokens per sequence: token i of sequence b sits at position
+// pos[b] (+ pos_offset) - (q_len - 1) + i.
+hipError_t launch_absorb(const gva_shape& s, int q_len, const float* q_nope,
+                         const float* q_rope, const float* M, const int32_t* pos, float scale,
+                         double base, float* qa, hipStream_t stream);
 
-hipError_t launch_append(const gva_shape& s, const float* v_new, const float* k_new,
+hipError_t launch_append(const gva_shape& s, int q_len, const float* v_new, const float* k_new,
                          const int32_t* pos, const int32_t* block_table, double base,
                          void* v_pool, void* k_pool, hipStream_t stream);
 
 // Absorption (q_nope != nullptr) and append (v_new != nullptr) in one launch;
-// the position of sequence b is pos[b] + pos_offset.
+// the last token of sequence b sits at position pos[b] + pos_offset.
 hipError_t launch_prologue(const gva_shape& s, const float* q_nope, const float* q_rope,
                            const float* M, float scale, float* qa, const float* v_new,
                            const float* k_new, const int32_t* block_table, void* v_pool,
-                           void* k_pool, const int32_t* pos, int pos_offset, double base,
-                           hipStream_t stream);
+                           void* k_pool, const int32_t* pos, int pos_offset, int q_len,
+                           double base, hipStream_t stream);
 
 // GVA decode (keys_separate = false: the key of head h is [V_g(h) | k_rope],
 // query already scaled) and GQA decode (keys_separate = true: key K_g(h),
 // query scaled by `scale` inside the kernel) share one launcher.
+// The decode launchers see H = query heads x query tokens (column h*L + i).
 struct DecodeArgs {
   const float* q;         // qa [B][H][d_h+d_r] or q [B][H][d_h]
   const void* v_pool;
@@ -63,6 +66,7 @@ struct DecodeArgs {
   float* out;
   float* lse;
   float q_scale;          // multiplies q inside the kernel
+  int q_len;              // query tokens per sequence (causal, the last q_len positions)
   bool keys_separate;
 };
 

@@ -37,12 +37,25 @@ struct PrologueArgs {
   const int32_t* block_table;
   void* v_pool;
   void* k_pool;
-  const int32_t* pos;  // position of sequence b: pos[b] + pos_offset
+  const int32_t* pos;  // position of sequence b's last token: pos[b] + pos_offset
   int pos_offset;
+  int q_len;           // tokens per sequence (L): token i sits at that position - (L-1) + i
   int B, H, G, d_h, d_n, d_r, bs, max_blocks, num_blocks;
   int absorb_blocks;   // blocks [0, absorb_blocks) absorb, the rest append
   int vec4;            // q_nope and M rows 16-byte aligned (d_n % 4 == 0)
 };
+
+// Rows are (sequence, token) pairs, r = b * L + i.  Per-head query rows are
+// laid out [B][H][L][*] and per-token rows [B][L][*]; token i of sequence b
+// sits at position pos[b] + pos_offset - (L - 1) + i.
+__device__ __forceinline__ size_t head_row(const PrologueArgs& a, int r, int h) {
+  const int b = r / a.q_len, i = r - b * a.q_len;
+  return (static_cast<size_t>(b) * a.H + h) * a.q_len + i;
+}
+__device__ __forceinline__ int row_pos(const PrologueArgs& a, int r) {
+  const int b = r / a.q_len, i = r - b * a.q_len;
+  return a.pos[b] + a.pos_offset - (a.q_len - 1) + i;
+}
 
 // Rotate (x0, x1) by angle pos * theta (float64).
 __device__ __forceinline__ void rotate_f64(double x0, double x1, int pos, double theta,
@@ -53,8 +66,8 @@ __device__ __forceinline__ void rotate_f64(double x0, double x1, int pos, double
   *y1 = x0 * s + x1 * c;
 }
 
-// Absorption, one 16 x 16 output tile per wave: sequences b0 .. b0+15 and
-// content dims e0 .. e0+15 of head h,
+// Absorption, one 16 x 16 output tile per wave: rows b0 .. b0+15 (one row
+// per sequence and query token) and content dims e0 .. e0+15 of head h,
 //   qa[b][h][e] = s * sum_n q_nope[b][h][n] M[h][e][n],
 // a (16 x d_n) x (d_n x 16) product on the fp32 matrix cores
 // (v_mfma_f32_16x16x4_f32: lane l feeds A[l%16][l/16] and B[l/16][l%16] and
@@ -70,6 +83,7 @@ __device__ __forceinline__ void absorb_block(const PrologueArgs& a, const RopeTa
   const int DT = a.d_h / 16;
   const int et = id % DT, rest = id / DT;
   const int h = rest % a.H, b0 = (rest / a.H) * 16;
+  const int R = a.B * a.q_len;  // rows
   const int li = lane & 15, kg = lane >> 4;
   const int half = a.d_r / 2;
   const int dq = a.d_h + a.d_r;
@@ -80,18 +94,18 @@ __device__ __forceinline__ void absorb_block(const PrologueArgs& a, const RopeTa
   const int hd = max(half, 1);
   int pi = et * 64 + lane;
   int p_seq = min(pi / hd, 15), p_i = pi % hd;
-  int p_b = min(b0 + p_seq, a.B - 1);
+  int p_b = min(b0 + p_seq, R - 1);
   float x0 = 0.f, x1 = 0.f;
   int p_pos = 0;
   if (half > 0) {  // uniform
-    const float* xr = a.q_rope + (static_cast<size_t>(p_b) * a.H + h) * a.d_r + 2 * p_i;
+    const float* xr = a.q_rope + head_row(a, p_b, h) * a.d_r + 2 * p_i;
     x0 = xr[0];
     x1 = xr[1];
-    p_pos = a.pos[p_b] + a.pos_offset;
+    p_pos = row_pos(a, p_b);
   }
 
-  const int bq = min(b0 + li, a.B - 1);
-  const float* qrow = a.q_nope + (static_cast<size_t>(bq) * a.H + h) * a.d_n;
+  const int bq = min(b0 + li, R - 1);
+  const float* qrow = a.q_nope + head_row(a, bq, h) * a.d_n;
   const float* mrow = a.M + (static_cast<size_t>(h) * a.d_h + et * 16 + li) * a.d_n;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (a.vec4) {
@@ -140,15 +154,15 @@ __device__ __forceinline__ void absorb_block(const PrologueArgs& a, const RopeTa
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int b = b0 + 4 * kg + r;
-    if (b < a.B) a.qa[(static_cast<size_t>(b) * a.H + h) * dq + et * 16 + li] = a.scale * acc[r];
+    if (b < R) a.qa[head_row(a, b, h) * dq + et * 16 + li] = a.scale * acc[r];
   }
 
   const double sc = static_cast<double>(a.scale);
   while (half > 0) {
-    if (pi < npairs && b0 + p_seq < a.B) {
+    if (pi < npairs && b0 + p_seq < R) {
       double y0, y1;
       rotate_f64(x0, x1, p_pos, rt.theta[p_i], &y0, &y1);
-      float* dst = a.qa + (static_cast<size_t>(p_b) * a.H + h) * dq + a.d_h + 2 * p_i;
+      float* dst = a.qa + head_row(a, p_b, h) * dq + a.d_h + 2 * p_i;
       dst[0] = static_cast<float>(sc * y0);
       dst[1] = static_cast<float>(sc * y1);
     }
@@ -156,11 +170,11 @@ __device__ __forceinline__ void absorb_block(const PrologueArgs& a, const RopeTa
     if (pi >= npairs) break;
     p_seq = pi / half;
     p_i = pi % half;
-    p_b = min(b0 + p_seq, a.B - 1);
-    const float* xr = a.q_rope + (static_cast<size_t>(p_b) * a.H + h) * a.d_r + 2 * p_i;
+    p_b = min(b0 + p_seq, R - 1);
+    const float* xr = a.q_rope + head_row(a, p_b, h) * a.d_r + 2 * p_i;
     x0 = xr[0];
     x1 = xr[1];
-    p_pos = a.pos[p_b] + a.pos_offset;
+    p_pos = row_pos(a, p_b);
   }
 }
 
@@ -176,8 +190,8 @@ __device__ __forceinline__ void store4(bf16_t* p, float x0, float x1, float x2, 
   *reinterpret_cast<uint2*>(p) = w;
 }
 
-// Append: one thread per four values or per rotary pair of one sequence's
-// new token.  Values are rounded once into the cache dtype; the positional
+// Append: one thread per four values or per rotary pair of one new token
+// (row r = b * L + i of v_new [B][L][G][d_h] and k_new [B][L][d_r]).  Values are rounded once into the cache dtype; the positional
 // key is rotated to its position in float64 and rounded once (the key is
 // cached already rotated: onedev.kr review, "How it differs").  A position
 // or block-table entry out of range skips the write.
@@ -186,26 +200,27 @@ __device__ __forceinline__ void append_block(const PrologueArgs& a, const RopeTa
                                              int id) {
   const int nv = a.G * a.d_h, nq = nv / 4, half = a.d_r / 2, per_b = nq + half;
   const int idx = id * kThreads + static_cast<int>(threadIdx.x);
-  if (idx >= a.B * per_b) return;
-  const int b = idx / per_b, r = idx - b * per_b;
+  if (idx >= a.B * a.q_len * per_b) return;
+  const int row = idx / per_b, r = idx - row * per_b;
+  const int b = row / a.q_len;
   const bool is_v = r < nq;
   const int i = r - nq;
   // all loads first: the position, then the four (or two) source scalars
-  const int p = a.pos[b] + a.pos_offset;
-  const float* s0 = is_v ? a.v_new + static_cast<size_t>(b) * nv + 4 * r
-                         : a.k_new + static_cast<size_t>(b) * a.d_r + 2 * i;
+  const int p = row_pos(a, row);
+  const float* s0 = is_v ? a.v_new + static_cast<size_t>(row) * nv + 4 * r
+                         : a.k_new + static_cast<size_t>(row) * a.d_r + 2 * i;
   const float* s1 = is_v ? s0 + 2 : s0;
   const float x0 = s0[0], x1 = s0[1], x2 = s1[0], x3 = s1[1];
   if (p < 0 || p >= a.max_blocks * a.bs) return;
   const int blk = a.block_table[static_cast<size_t>(b) * a.max_blocks + p / a.bs];
   if (blk < 0 || blk >= a.num_blocks) return;
-  const size_t row = static_cast<size_t>(blk) * a.bs + (p % a.bs);
+  const size_t slot = static_cast<size_t>(blk) * a.bs + (p % a.bs);
   if (is_v) {
-    store4(static_cast<CT*>(a.v_pool) + row * nv + 4 * r, x0, x1, x2, x3);
+    store4(static_cast<CT*>(a.v_pool) + slot * nv + 4 * r, x0, x1, x2, x3);
   } else {
     double y0, y1;
     rotate_f64(x0, x1, p, rt.theta[i], &y0, &y1);
-    CT* k = static_cast<CT*>(a.k_pool) + row * a.d_r + 2 * i;
+    CT* k = static_cast<CT*>(a.k_pool) + slot * a.d_r + 2 * i;
     k[0] = Cache<CT>::from_f64(y0);
     k[1] = Cache<CT>::from_f64(y1);
   }
@@ -232,12 +247,13 @@ RopeTable rope_table(int d_r, double base) {
 hipError_t launch_prologue(const gva_shape& s, const float* q_nope, const float* q_rope,
                            const float* M, float scale, float* qa, const float* v_new,
                            const float* k_new, const int32_t* block_table, void* v_pool,
-                           void* k_pool, const int32_t* pos, int pos_offset, double base,
-                           hipStream_t stream) {
-  if (s.d_h % 16 || s.d_r / 2 > kMaxHalfRope || s.d_r < 0 || s.d_r % 2)
+                           void* k_pool, const int32_t* pos, int pos_offset, int q_len,
+                           double base, hipStream_t stream) {
+  if (s.d_h % 16 || s.d_r / 2 > kMaxHalfRope || s.d_r < 0 || s.d_r % 2 || q_len < 1)
     return hipErrorInvalidValue;
   PrologueArgs a{};
   a.pos_offset = pos_offset;
+  a.q_len = q_len;
   a.q_nope = q_nope;
   a.q_rope = q_rope;
   a.M = M;
@@ -258,11 +274,11 @@ hipError_t launch_prologue(const gva_shape& s, const float* q_nope, const float*
   a.bs = s.block_size;
   a.max_blocks = s.max_blocks;
   a.num_blocks = s.num_blocks;
-  a.absorb_blocks = q_nope ? s.H * ((s.B + 15) / 16) * (s.d_h / 16) : 0;
+  const long long rows = static_cast<long long>(s.B) * q_len;
+  a.absorb_blocks = q_nope ? static_cast<int>(s.H * ((rows + 15) / 16) * (s.d_h / 16)) : 0;
   a.vec4 = q_nope && s.d_n % 4 == 0 && reinterpret_cast<uintptr_t>(q_nope) % 16 == 0 &&
            reinterpret_cast<uintptr_t>(M) % 16 == 0;
-  const long long append_items =
-      v_new ? static_cast<long long>(s.B) * (s.G * s.d_h / 4 + s.d_r / 2) : 0;
+  const long long append_items = v_new ? rows * (s.G * s.d_h / 4 + s.d_r / 2) : 0;
   const int blocks = a.absorb_blocks + static_cast<int>((append_items + kThreads - 1) / kThreads);
   if (blocks == 0) return hipSuccess;
   const RopeTable rt = rope_table(s.d_r, base);
@@ -273,18 +289,18 @@ hipError_t launch_prologue(const gva_shape& s, const float* q_nope, const float*
   return hipGetLastError();
 }
 
-hipError_t launch_absorb(const gva_shape& s, const float* q_nope, const float* q_rope,
-                         const float* M, const int32_t* pos, float scale, double base,
-                         float* qa, hipStream_t stream) {
+hipError_t launch_absorb(const gva_shape& s, int q_len, const float* q_nope,
+                         const float* q_rope, const float* M, const int32_t* pos, float scale,
+                         double base, float* qa, hipStream_t stream) {
   return launch_prologue(s, q_nope, q_rope, M, scale, qa, nullptr, nullptr, nullptr, nullptr,
-                         nullptr, pos, 0, base, stream);
+                         nullptr, pos, 0, q_len, base, stream);
 }
 
-hipError_t launch_append(const gva_shape& s, const float* v_new, const float* k_new,
+hipError_t launch_append(const gva_shape& s, int q_len, const float* v_new, const float* k_new,
                          const int32_t* pos, const int32_t* block_table, double base,
                          void* v_pool, void* k_pool, hipStream_t stream) {
   return launch_prologue(s, nullptr, nullptr, nullptr, 0.f, nullptr, v_new, k_new, block_table,
-                         v_pool, k_pool, pos, 0, base, stream);
+                         v_pool, k_pool, pos, 0, q_len, base, stream);
 }
 
 }  // namespace gva

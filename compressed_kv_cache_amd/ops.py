@@ -264,3 +264,146 @@ def decode_step(q_nope, q_rope, M, v_pool, k_pool, block_table, seq_lens, max_se
         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(dev))
     check("gva_decode_step", st)
     return out, lse
+
+
+# ---- several tokens per sequence (q_len = L): the *_multi entry points ----
+
+def absorb_query_multi(q_nope, q_rope, M, pos, softmax_scale=None, rope_base=10000.0,
+                       out=None):
+    """qa[B,H,L,d_h+d_r] for L query tokens per sequence; pos[b] is the
+    position of the last one (gva_absorb_query_multi)."""
+    dev = q_nope.device
+    _need(q_nope, "q_nope", torch.float32, dev, 4)
+    B, H, L, d_n = q_nope.shape
+    _need(q_rope, "q_rope", torch.float32, dev, 4)
+    _need(M, "M", torch.float32, dev, 3)
+    _need(pos, "pos", torch.int32, dev, 1)
+    d_r = q_rope.shape[3]
+    d_h = M.shape[1]
+    if tuple(q_rope.shape[:3]) != (B, H, L) or tuple(M.shape) != (H, d_h, d_n) \
+            or pos.shape[0] != B:
+        raise ValueError("inconsistent shapes for absorb_query_multi")
+    if out is None:
+        out = torch.empty((B, H, L, d_h + d_r), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev, 4)
+    s = make_shape(B, H, 1, d_h, d_n, d_r)
+    st = _lib.load().gva_absorb_query_multi(
+        ctypes.byref(s), L, _ptr(q_nope), _ptr(q_rope), _ptr(M), _ptr(pos),
+        float(softmax_scale or 0.0), float(rope_base), _ptr(out), _stream(dev))
+    check("gva_absorb_query_multi", st)
+    return out
+
+
+def append_cache_multi(v_new, k_new, pos, block_table, v_pool, k_pool, rope_base=10000.0):
+    """Write L new tokens per sequence (v_new [B,L,G,d_h], k_new [B,L,d_r]);
+    pos[b] is the position of the last one (gva_append_cache_multi)."""
+    dev = v_pool.device
+    _need(v_new, "v_new", torch.float32, dev, 4)
+    _need(k_new, "k_new", torch.float32, dev, 3)
+    _need(pos, "pos", torch.int32, dev, 1)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    cdt = _cache_dtype(v_pool, "v_pool")
+    _need(v_pool, "v_pool", v_pool.dtype, dev, 4)
+    _need(k_pool, "k_pool", v_pool.dtype, dev, 3)
+    NB, bs, G, d_h = v_pool.shape
+    B, L = v_new.shape[:2]
+    d_r = k_pool.shape[2]
+    if tuple(v_new.shape) != (B, L, G, d_h) or tuple(k_new.shape) != (B, L, d_r) \
+            or k_pool.shape[0] != NB or k_pool.shape[1] != bs \
+            or block_table.shape[0] != B or pos.shape[0] != B:
+        raise ValueError("inconsistent shapes for append_cache_multi")
+    s = GvaShape(B, G, G, d_h, 1, d_r, bs, block_table.shape[1], NB, cdt)
+    st = _lib.load().gva_append_cache_multi(
+        ctypes.byref(s), L, _ptr(v_new), _ptr(k_new), _ptr(pos), _ptr(block_table),
+        float(rope_base), _ptr(v_pool), _ptr(k_pool), _stream(dev))
+    check("gva_append_cache_multi", st)
+
+
+def decode_workspace_bytes_multi(B, H, q_len, v_pool, k_pool, block_table, max_seq_len):
+    """Workspace size gva_decode_attention_multi needs (zero-fill once)."""
+    s = _decode_shape(B, H, v_pool, k_pool.shape[2], block_table)
+    n = ctypes.c_size_t(0)
+    check("gva_decode_workspace_size_multi", _lib.load().gva_decode_workspace_size_multi(
+        ctypes.byref(s), int(q_len), int(max_seq_len), ctypes.byref(n)))
+    return n.value
+
+
+def decode_attention_multi(qa, v_pool, k_pool, block_table, seq_lens, max_seq_len,
+                           workspace=None, out=None, lse=None, want_lse=True):
+    """out[B,H,L,d_h] (and lse[B,H,L]) of L absorbed queries per sequence,
+    query i at position seq_lens-L+i attending causally
+    (gva_decode_attention_multi)."""
+    dev = qa.device
+    _need(qa, "qa", torch.float32, dev, 4)
+    _need(v_pool, "v_pool", v_pool.dtype, dev, 4)
+    _need(k_pool, "k_pool", v_pool.dtype, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    B, H, L, dq = qa.shape
+    d_h, d_r = v_pool.shape[3], k_pool.shape[2]
+    if dq != d_h + d_r or block_table.shape[0] != B or seq_lens.shape[0] != B \
+            or k_pool.shape[:2] != v_pool.shape[:2]:
+        raise ValueError("inconsistent shapes for decode_attention_multi")
+    s = _decode_shape(B, H, v_pool, d_r, block_table)
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    check("gva_decode_workspace_size_multi", lib.gva_decode_workspace_size_multi(
+        ctypes.byref(s), L, int(max_seq_len), ctypes.byref(n)))
+    workspace = _workspace(n.value, dev, workspace)
+    if out is None:
+        out = torch.empty((B, H, L, d_h), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=dev)
+    st = lib.gva_decode_attention_multi(
+        ctypes.byref(s), L, _ptr(qa), _ptr(v_pool), _ptr(k_pool), _ptr(block_table),
+        _ptr(seq_lens), int(max_seq_len), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(dev))
+    check("gva_decode_attention_multi", st)
+    return out, lse
+
+
+def decode_step_multi(q_nope, q_rope, M, v_pool, k_pool, block_table, seq_lens, max_seq_len,
+                      v_new=None, k_new=None, softmax_scale=None, rope_base=10000.0,
+                      workspace=None, out=None, lse=None, want_lse=True):
+    """Append L new tokens (if v_new/k_new are given) + absorb L queries +
+    causal decode (gva_decode_step_multi); seq_lens counts the new tokens."""
+    dev = v_pool.device
+    _need(q_nope, "q_nope", torch.float32, dev, 4)
+    _need(q_rope, "q_rope", torch.float32, dev, 4)
+    _need(M, "M", torch.float32, dev, 3)
+    _need(v_pool, "v_pool", v_pool.dtype, dev, 4)
+    _need(k_pool, "k_pool", v_pool.dtype, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    B, H, L, d_n = q_nope.shape
+    NB, bs, G, d_h = v_pool.shape
+    d_r = q_rope.shape[3]
+    if tuple(q_rope.shape[:3]) != (B, H, L) or tuple(M.shape) != (H, d_h, d_n) \
+            or tuple(k_pool.shape) != (NB, bs, d_r) or block_table.shape[0] != B \
+            or seq_lens.shape[0] != B:
+        raise ValueError("inconsistent shapes for decode_step_multi")
+    if (v_new is None) != (k_new is None):
+        raise ValueError("give both v_new and k_new, or neither")
+    if v_new is not None:
+        _need(v_new, "v_new", torch.float32, dev, 4)
+        _need(k_new, "k_new", torch.float32, dev, 3)
+        if tuple(v_new.shape) != (B, L, G, d_h) or tuple(k_new.shape) != (B, L, d_r):
+            raise ValueError("inconsistent shapes for v_new / k_new")
+    s = GvaShape(B, H, G, d_h, d_n, d_r, bs, block_table.shape[1], NB,
+                 _cache_dtype(v_pool, "v_pool"))
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    check("gva_decode_step_workspace_size_multi", lib.gva_decode_step_workspace_size_multi(
+        ctypes.byref(s), L, int(max_seq_len), ctypes.byref(n)))
+    workspace = _workspace(n.value, dev, workspace)
+    if out is None:
+        out = torch.empty((B, H, L, d_h), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=dev)
+    st = lib.gva_decode_step_multi(
+        ctypes.byref(s), L, _ptr(q_nope), _ptr(q_rope), _ptr(M), float(softmax_scale or 0.0),
+        float(rope_base), _ptr(v_new), _ptr(k_new), _ptr(v_pool), _ptr(k_pool),
+        _ptr(block_table), _ptr(seq_lens), int(max_seq_len), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(dev))
+    check("gva_decode_step_multi", st)
+    return out, lse

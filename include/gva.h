@@ -40,6 +40,10 @@
  *             slot j%bs.  A contiguous cache is the identity table.
  *   Positions 0-based.  In decode the query token is the last cached token
  *             of its sequence (position seq_lens[b]-1) and attends to itself.
+ *             The *_multi entry points take q_len = L tokens per sequence:
+ *             token i sits at position (last position) - (L-1) + i, and in
+ *             decode query i (position seq_lens[b]-L+i) attends causally to
+ *             positions 0 .. seq_lens[b]-L+i.
  *   Heads     Query head h reads value group g(h) = h / (H/G).
  */
 #ifndef GVA_H
@@ -52,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GVA_ABI_VERSION 1
+#define GVA_ABI_VERSION 2
 
 typedef enum gva_status {
   GVA_OK = 0,
@@ -194,6 +198,60 @@ gva_status gva_decode_step(const gva_shape* shape, const float* q_nope,
                            int32_t max_seq_len, void* workspace,
                            size_t workspace_bytes, float* out, float* lse,
                            void* stream);
+
+/* Several tokens per sequence (q_len = L, 1 <= L <= 64): the entry points
+ * above with one more size.  Each query token is absorbed on its own, once
+ * per head and token (onedev.kr review, "How it works"), and attends
+ * causally; L = 1 is exactly the single-token call.  Layouts:
+ *   q_nope [B][H][L][d_n], q_rope [B][H][L][d_r], qa [B][H][L][d_h + d_r],
+ *   out [B][H][L][d_h], lse [B][H][L]      (query token i of head h);
+ *   v_new [B][L][G][d_h], k_new [B][L][d_r] (new token i of sequence b).
+ * gva_absorb_query_multi: pos[b] is the position of the LAST query token;
+ *   token i is rotated to pos[b] - (L-1) + i.
+ * gva_append_cache_multi: pos[b] is the position of the LAST new token;
+ *   token i is written at pos[b] - (L-1) + i.
+ * gva_decode_attention_multi: query i of sequence b sits at position
+ *   seq_lens[b] - L + i and scores positions j <= seq_lens[b] - L + i only.
+ *   0 < seq_lens[b] < L is invalid (NaN outputs, like other bad lengths).
+ * gva_decode_step_multi: append the L new tokens (when v_new/k_new are
+ *   given), absorb the L queries, decode; seq_lens already counts the new
+ *   tokens.
+ * Other arguments, errors and workspace rules as the single-token calls;
+ * q_len < 1 is GVA_ERR_SHAPE, q_len > 64 GVA_ERR_UNSUPPORTED. */
+gva_status gva_absorb_query_multi(const gva_shape* shape, int32_t q_len,
+                                  const float* q_nope, const float* q_rope,
+                                  const float* M, const int32_t* pos,
+                                  float softmax_scale, float rope_base,
+                                  float* qa, void* stream);
+gva_status gva_append_cache_multi(const gva_shape* shape, int32_t q_len,
+                                  const float* v_new, const float* k_new,
+                                  const int32_t* pos,
+                                  const int32_t* block_table, float rope_base,
+                                  void* v_pool, void* k_pool, void* stream);
+gva_status gva_decode_workspace_size_multi(const gva_shape* shape,
+                                           int32_t q_len, int32_t max_seq_len,
+                                           size_t* bytes);
+gva_status gva_decode_attention_multi(const gva_shape* shape, int32_t q_len,
+                                      const float* qa, const void* v_pool,
+                                      const void* k_pool,
+                                      const int32_t* block_table,
+                                      const int32_t* seq_lens,
+                                      int32_t max_seq_len, void* workspace,
+                                      size_t workspace_bytes, float* out,
+                                      float* lse, void* stream);
+gva_status gva_decode_step_workspace_size_multi(const gva_shape* shape,
+                                                int32_t q_len,
+                                                int32_t max_seq_len,
+                                                size_t* bytes);
+gva_status gva_decode_step_multi(const gva_shape* shape, int32_t q_len,
+                                 const float* q_nope, const float* q_rope,
+                                 const float* M, float softmax_scale,
+                                 float rope_base, const float* v_new,
+                                 const float* k_new, void* v_pool,
+                                 void* k_pool, const int32_t* block_table,
+                                 const int32_t* seq_lens, int32_t max_seq_len,
+                                 void* workspace, size_t workspace_bytes,
+                                 float* out, float* lse, void* stream);
 
 /* Same-shape grouped-query attention decode, the baseline GVA is compared
  * with: each group stores both a key and a value row per token

@@ -37,7 +37,11 @@ Readings of points the pages leave open:
 * positions are 0-based; the query token sits at position len-1 and attends
   to itself; a sequence of length 0 gives out = 0, lse = -inf;
 * appended values are rounded to the cache dtype once, to nearest-even, from
-  the exact (float64) rotated key.
+  the exact (float64) rotated key;
+* several query tokens per sequence (q_len = L): they are the last L cached
+  positions, query i sits at position len-L+i and attends causally to
+  positions 0 .. len-L+i (each query token is absorbed separately, once per
+  head and token).
 """
 import math
 
@@ -49,7 +53,8 @@ __all__ = [
     "head_group", "default_scale", "softmax_attention", "gather_tokens",
     "reconstruct_keys", "gva_decode_materialized", "absorb_query",
     "attend_absorbed", "append_token", "gqa_decode", "chunk_partials",
-    "merge_partials",
+    "merge_partials", "query_positions", "gva_decode_materialized_queries",
+    "absorb_queries", "attend_absorbed_queries", "append_tokens",
 ]
 
 
@@ -356,6 +361,115 @@ def gqa_decode(q, k_pool, v_pool, block_table, seq_lens, scale=None,
                                             V_all[:, g, :], scale)
             out[b, h], lse[b, h] = o, ls
     return out, lse
+
+
+# --------------------------------------------------------------------------
+# Several query tokens per sequence
+# --------------------------------------------------------------------------
+
+def query_positions(seq_len, q_len):
+    """Positions of the q_len query tokens of a sequence whose cache holds
+    seq_len tokens: the last q_len positions, seq_len-q_len .. seq_len-1."""
+    return np.arange(int(seq_len) - int(q_len), int(seq_len))
+
+
+def gva_decode_materialized_queries(q_nope, q_rope, M, v_pool, k_pool,
+                                    block_table, seq_lens, scale=None,
+                                    base=10000.0, block_size=64, seqs=None,
+                                    heads=None):
+    """GVA decode of L query tokens per sequence, keys materialised.
+
+    q_nope [B, H, L, d_n], q_rope [B, H, L, d_r].  Query token i of sequence
+    b sits at position t = len_b - L + i and sees cached positions 0..t
+    (causal); for each head h it is the single-query definition of
+    ``gva_decode_materialized`` with the context cut at t + 1 and R_t applied
+    to its position slice.  Returns out [B, H, L, d_h], lse [B, H, L]."""
+    q_nope, q_rope, M = to_f64(q_nope), to_f64(q_rope), to_f64(M)
+    v_pool, k_pool = to_f64(v_pool), to_f64(k_pool)
+    block_table = np.asarray(block_table)
+    seq_lens = np.asarray(seq_lens).astype(np.int64)
+    B, H, L, d_n = q_nope.shape
+    d_r = q_rope.shape[-1]
+    G, d_h = v_pool.shape[2], v_pool.shape[3]
+    if scale is None:
+        scale = default_scale(d_n, d_r)
+    out = np.full((B, H, L, d_h), np.nan)
+    lse = np.full((B, H, L), np.nan)
+    for b in _select(B, seqs):
+        n = int(seq_lens[b])
+        V_all = gather_tokens(v_pool, block_table[b], n, block_size)
+        k_all = gather_tokens(k_pool, block_table[b], n, block_size)
+        for h in _select(H, heads):
+            g = head_group(h, H, G)
+            K_h = reconstruct_keys(V_all[:, g, :], M[h])
+            keys = np.concatenate([K_h, k_all], axis=1)
+            for i, t in enumerate(query_positions(n, L)):
+                q_r = rope_rotate(q_rope[b, h, i], t, base)
+                query = np.concatenate([q_nope[b, h, i], q_r])
+                o, ls, _, _ = softmax_attention(query, keys[:t + 1],
+                                                V_all[:t + 1, g, :], scale)
+                out[b, h, i], lse[b, h, i] = o, ls
+    return out, lse
+
+
+def absorb_queries(q_nope, q_rope, M, pos_last, scale=None, base=10000.0):
+    """Absorbed queries of L tokens per sequence: qa[b, h, i] is
+    ``absorb_query`` of token i at position pos_last[b] - L + 1 + i.
+    q_nope [B, H, L, d_n], q_rope [B, H, L, d_r] -> qa [B, H, L, d_h+d_r]."""
+    q_nope, q_rope, M = to_f64(q_nope), to_f64(q_rope), to_f64(M)
+    pos_last = np.asarray(pos_last).astype(np.float64)
+    B, H, L, d_n = q_nope.shape
+    d_r = q_rope.shape[-1]
+    if scale is None:
+        scale = default_scale(d_n, d_r)
+    q_tilde = np.einsum("bhin,hen->bhie", q_nope, M)
+    pos = pos_last[:, None] - (L - 1) + np.arange(L)[None, :]      # [B, L]
+    q_r = rope_rotate(q_rope, pos[:, None, :], base)
+    return scale * np.concatenate([q_tilde, q_r], axis=-1)
+
+
+def attend_absorbed_queries(qa, v_pool, k_pool, block_table, seq_lens,
+                            block_size=64, seqs=None, heads=None):
+    """Causal attention of L absorbed queries per sequence over the value
+    cache: query i of sequence b (position len_b - L + i) scores
+    <qa[b,h,i], [V[b,j,g(h)] | k_rope[b,j]]> for j <= its position.
+    qa [B, H, L, d_h+d_r] -> out [B, H, L, d_h], lse [B, H, L]."""
+    qa = to_f64(qa)
+    v_pool, k_pool = to_f64(v_pool), to_f64(k_pool)
+    block_table = np.asarray(block_table)
+    seq_lens = np.asarray(seq_lens).astype(np.int64)
+    B, H, L, _ = qa.shape
+    G, d_h = v_pool.shape[2], v_pool.shape[3]
+    out = np.full((B, H, L, d_h), np.nan)
+    lse = np.full((B, H, L), np.nan)
+    for b in _select(B, seqs):
+        n = int(seq_lens[b])
+        V_all = gather_tokens(v_pool, block_table[b], n, block_size)
+        k_all = gather_tokens(k_pool, block_table[b], n, block_size)
+        for h in _select(H, heads):
+            g = head_group(h, H, G)
+            keys = np.concatenate([V_all[:, g, :], k_all], axis=1)
+            for i, t in enumerate(query_positions(n, L)):
+                o, ls, _, _ = softmax_attention(qa[b, h, i], keys[:t + 1],
+                                                V_all[:t + 1, g, :], 1.0)
+                out[b, h, i], lse[b, h, i] = o, ls
+    return out, lse
+
+
+def append_tokens(v_pool, k_pool, v_new, k_new, pos_last, block_table,
+                  base=10000.0, block_size=64, cache_dtype="bfloat16"):
+    """Write L new tokens per sequence: token i of sequence b goes to position
+    pos_last[b] - L + 1 + i, exactly as ``append_token`` writes one token.
+    v_new [B, L, G, d_h], k_new [B, L, d_r] (unrotated)."""
+    v_new, k_new = to_f64(v_new), to_f64(k_new)
+    pos_last = np.asarray(pos_last).astype(np.int64)
+    L = v_new.shape[1]
+    for i in range(L):
+        v_pool, k_pool = append_token(v_pool, k_pool, v_new[:, i], k_new[:, i],
+                                      pos_last - (L - 1) + i, block_table,
+                                      base=base, block_size=block_size,
+                                      cache_dtype=cache_dtype)
+    return v_pool, k_pool
 
 
 # --------------------------------------------------------------------------

@@ -5,8 +5,8 @@ Shared by the float64 oracle (``oracle/``) and the HIP path
 """
 from .configs import CONFIGS, CONFIG_ORDER, GVAConfig, get_config
 from .inputs import (block_layout, draw_seq_lens, make_gqa_inputs,
-                     make_gva_inputs, with_overrides)
+                     make_gva_inputs, make_gva_multi_inputs, with_overrides)
 
 __all__ = ["CONFIGS", "CONFIG_ORDER", "GVAConfig", "get_config",
            "block_layout", "draw_seq_lens", "make_gqa_inputs",
-           "make_gva_inputs", "with_overrides"]
+           "make_gva_inputs", "make_gva_multi_inputs", "with_overrides"]

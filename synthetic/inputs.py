@@ -20,7 +20,10 @@ Recipe (Grouped Value Attention pages; the values are standard normal):
   to sequences in order from a random permutation (shuffled tables) or from
   ``arange`` (contiguous tables); unused table entries are 0;
 * workloads that append draw ``v_new[B,G,d_h]`` and the unrotated
-  ``k_new[B,d_r]`` ~ N(0, 1) and poison the slot being appended with NaN.
+  ``k_new[B,d_r]`` ~ N(0, 1) and poison the slot being appended with NaN;
+* with L query tokens per sequence the queries are ``[B,H,L,d_n]`` and
+  ``[B,H,L,d_r]``, the new tokens ``[B,L,G,d_h]`` and ``[B,L,d_r]`` (the last
+  L positions), all ~ N(0, 1) from their own streams.
 """
 import math
 from typing import Dict, Optional
@@ -33,6 +36,7 @@ from .configs import GVAConfig
 _STREAM = {
     "q_nope": 1, "q_rope": 2, "M": 3, "lens": 4, "perm": 5, "v_pool": 6,
     "k_pool": 7, "v_new": 8, "k_new": 9, "gqa_q": 10, "gqa_k": 11,
+    "mq_nope": 12, "mq_rope": 13, "mv_new": 14, "mk_new": 15,
 }
 
 _TORCH_DTYPE = {"float32": torch.float32, "bfloat16": torch.bfloat16}
@@ -152,6 +156,38 @@ def make_gva_inputs(cfg: GVAConfig, device="cpu", seed: Optional[int] = None,
     out["block_table_host"] = table_cpu
     out["num_blocks"] = nb
     out["max_seq_len"] = max(lens) if lens else 0
+    return out
+
+
+def make_gva_multi_inputs(cfg: GVAConfig, q_len: int, device="cpu",
+                          seed: Optional[int] = None,
+                          seq_lens: Optional[torch.Tensor] = None,
+                          shuffled: Optional[bool] = None) -> Dict[str, object]:
+    """Inputs of a decode step with ``q_len`` query tokens per sequence: the
+    caches, lengths and maps of ``make_gva_inputs`` (without its one-token
+    append), plus ``q_nope[B,H,L,d_n]``, ``q_rope[B,H,L,d_r]`` and, when the
+    workload appends, ``v_new[B,L,G,d_h]`` and ``k_new[B,L,d_r]`` for the last
+    L positions of each sequence (those slots poisoned with NaN).  ``pos`` is
+    the position of each sequence's last token."""
+    seed = cfg.seed if seed is None else seed
+    dev = torch.device(device)
+    base = with_overrides(cfg, append=False)
+    out = make_gva_inputs(base, device=device, seed=seed, seq_lens=seq_lens,
+                          shuffled=shuffled)
+    out["cfg"] = cfg
+    B, H, G, d_h, d_n, d_r, bs = (cfg.B, cfg.H, cfg.G, cfg.d_h, cfg.d_n,
+                                  cfg.d_r, cfg.block_size)
+    L = int(q_len)
+    out["q_len"] = L
+    out["q_nope"] = _randn((B, H, L, d_n), dev, seed, "mq_nope")
+    out["q_rope"] = _randn((B, H, L, d_r), dev, seed, "mq_rope")
+    if cfg.append:
+        out["v_new"] = _randn((B, L, G, d_h), dev, seed, "mv_new")
+        out["k_new"] = _randn((B, L, d_r), dev, seed, "mk_new")
+        lens = [int(x) for x in out["seq_lens_host"].tolist()]
+        extra = [(b, p) for b, n in enumerate(lens) for p in range(max(0, n - L), n)]
+        _poison_tail(out["v_pool"], out["block_table_host"], lens, bs, extra)
+        _poison_tail(out["k_pool"], out["block_table_host"], lens, bs, extra)
     return out
 
 

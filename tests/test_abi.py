@@ -33,7 +33,10 @@ def test_header_declares_expected_entry_points():
     for n in ("gva_absorb_query", "gva_append_cache", "gva_decode_attention",
               "gva_decode_workspace_size", "gqa_decode_attention",
               "gqa_decode_workspace_size", "gva_cache_scalars_per_token",
-              "gva_status_string", "gva_abi_version"):
+              "gva_status_string", "gva_abi_version", "gva_absorb_query_multi",
+              "gva_append_cache_multi", "gva_decode_workspace_size_multi",
+              "gva_decode_attention_multi", "gva_decode_step_workspace_size_multi",
+              "gva_decode_step_multi"):
         assert n in names
 
 
@@ -47,7 +50,7 @@ def test_library_exports_every_declared_symbol(g):
 
 
 def test_version_and_status_strings(g):
-    assert g.lib.gva_abi_version() == 1
+    assert g.lib.gva_abi_version() == 2
     for code in range(7):
         assert g.lib.gva_status_string(code)
     assert g.lib.gva_status_string(99) == b"unknown status"
@@ -195,3 +198,58 @@ def test_launch_without_device_reports_hip_error(g):
     st = g.lib.gva_absorb_query(ctypes.byref(s), P(0x10000), P(0x10000), P(0x10000),
                                 P(0x10000), 0.0, 1e4, P(0x10000), None)
     assert st == 6
+
+
+# ---- several query tokens per sequence ----
+
+def _ws_multi(g, s, q_len, max_seq_len=256):
+    n = ctypes.c_size_t(0)
+    st = g.lib.gva_decode_workspace_size_multi(ctypes.byref(s), q_len, max_seq_len,
+                                               ctypes.byref(n))
+    return st, n.value
+
+
+def test_multi_workspace_validates_q_len(g):
+    s = _shape(g)
+    assert _ws_multi(g, s, 0)[0] == 2
+    assert _ws_multi(g, s, -3)[0] == 2
+    assert _ws_multi(g, s, 65)[0] == 3
+    st1, n1 = _ws_multi(g, s, 1)
+    assert (st1, n1) == _ws(g, s)          # q_len = 1 is the single-token call
+    st4, n4 = _ws_multi(g, s, 4)
+    assert st4 == 0 and n4 > n1            # one partial record per query token
+
+
+def test_multi_step_workspace_holds_all_absorbed_queries(g):
+    s = _shape(g)
+    n1, n4 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert g.lib.gva_decode_step_workspace_size_multi(ctypes.byref(s), 1, 256,
+                                                      ctypes.byref(n1)) == 0
+    n0 = ctypes.c_size_t(0)
+    assert g.lib.gva_decode_step_workspace_size(ctypes.byref(s), 256, ctypes.byref(n0)) == 0
+    assert n0.value == n1.value
+    assert g.lib.gva_decode_step_workspace_size_multi(ctypes.byref(s), 4, 256,
+                                                      ctypes.byref(n4)) == 0
+    qa4 = s.B * s.H * 4 * (s.d_h + s.d_r) * 4
+    assert n4.value >= qa4
+
+
+def test_multi_entry_points_validate(g):
+    P = ctypes.c_void_p
+    s = _shape(g)
+    args = [P(0x10000)] * 4
+    f = g.lib.gva_absorb_query_multi
+    assert f(ctypes.byref(s), 0, *args, 0.0, 1e4, P(0x10000), None) == 2
+    assert f(ctypes.byref(s), 2, *args, 0.0, 1e4, P(None), None) == 1
+    a = g.lib.gva_append_cache_multi
+    ptr = [P(0x10000)] * 4
+    assert a(ctypes.byref(s), 0, *ptr, 1e4, P(0x1000), P(0x1000), None) == 2
+    assert a(ctypes.byref(s), 2, *ptr, 1e4, P(None), P(0x1000), None) == 1
+    d = g.lib.gva_decode_attention_multi
+    assert d(ctypes.byref(s), 0, P(0x10000), P(0x20000), P(0x30000), P(0x40000),
+             P(0x50000), 128, P(0x60000), 1 << 30, P(0x70000), P(None), None) == 2
+    assert d(ctypes.byref(s), 4, P(None), P(0x20000), P(0x30000), P(0x40000),
+             P(0x50000), 128, P(0x60000), 1 << 30, P(0x70000), P(None), None) == 1
+    _, need = _ws_multi(g, s, 4, 128)
+    assert d(ctypes.byref(s), 4, P(0x10000), P(0x20000), P(0x30000), P(0x40000),
+             P(0x50000), 128, P(0x60000), need - 1, P(0x70000), P(None), None) == 5

@@ -507,3 +507,139 @@ def test_additive_head_split(g, gpu):
         h["q_nope"], h["q_rope"], h["M"], h["v_pool"], h["k_pool"], h["block_table"],
         h["seq_lens"], base=cfg.rope_base)
     assert_bf16_parity(cpu(out).double().numpy(), ref)
+
+
+# ------------------------------------------ several query tokens (L > 1) ----
+
+MULTI_LENS = [4, 5, 63, 64, 65, 66, 67, 128, 129, 1000]
+
+
+def _multi_case(gpu, H, G, d_h, d_n, d_r, dtype, L, lens=MULTI_LENS, append=False):
+    base = syn.get_config("long_ragged")
+    cfg = syn.with_overrides(base, B=len(lens), H=H, G=G, d_h=d_h, d_n=d_n, d_r=d_r,
+                             cache_dtype=dtype, len_range=None, T=None, append=append)
+    x = syn.make_gva_multi_inputs(cfg, L, device=gpu,
+                                  seq_lens=torch.tensor(lens, dtype=torch.int32),
+                                  shuffled=True)
+    h = {k: cpu(v) for k, v in x.items() if isinstance(v, torch.Tensor)}
+    return cfg, x, h
+
+
+@pytest.mark.parametrize("H,G,d_h,d_n,d_r,dtype,L", [
+    (16, 4, 64, 48, 16, "bfloat16", 4),     # matrix cores, one group per head tile
+    (16, 4, 64, 48, 16, "bfloat16", 2),     # matrix cores, two groups per head tile
+    (16, 4, 64, 40, 24, "bfloat16", 4),
+    (32, 8, 128, 96, 32, "bfloat16", 2),    # matrix cores, d_h 128
+    (16, 4, 64, 64, 0, "bfloat16", 4),      # no positional slice
+    (8, 8, 32, 24, 8, "float32", 3),        # vector path
+    (16, 4, 64, 48, 16, "float32", 4),      # vector path, fp32 cache
+])
+def test_multi_query_decode(g, gpu, H, G, d_h, d_n, d_r, dtype, L):
+    """L query tokens per sequence (positions len-L .. len-1), each attending
+    causally; lengths put the causal tail across 64-token chunk edges."""
+    cfg, x, h = _multi_case(gpu, H, G, d_h, d_n, d_r, dtype, L)
+    announce("multi-query decode", H, G, d_h, d_r, dtype, "L", L)
+    qa = g.absorb_query_multi(x["q_nope"], x["q_rope"], x["M"], x["pos"],
+                              rope_base=cfg.rope_base)
+    out, lse = g.decode_attention_multi(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                        x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    ref_qa = o.absorb_queries(h["q_nope"], h["q_rope"], h["M"], h["pos"],
+                              base=cfg.rope_base)
+    assert_fp32_parity(cpu(qa), ref_qa, tol=1e-6, what="qa")
+    ref, ref_lse = o.gva_decode_materialized_queries(
+        h["q_nope"], h["q_rope"], h["M"], h["v_pool"], h["k_pool"], h["block_table"],
+        h["seq_lens"], base=cfg.rope_base)
+    if dtype == "float32":
+        assert_fp32_parity(cpu(out), ref)
+        assert_fp32_parity(cpu(lse), ref_lse)
+    else:
+        assert_bf16_parity(cpu(out).double().numpy(), ref)
+        np.testing.assert_allclose(cpu(lse).double().numpy(), ref_lse, rtol=0, atol=1e-3)
+
+
+@pytest.mark.parametrize("L", [2, 4])
+def test_multi_query_step_with_append(g, gpu, L):
+    """gva_decode_step_multi: the L new tokens are appended (values bit for bit,
+    rotated keys as the oracle rounds them), then the L queries attend."""
+    cfg, x, h = _multi_case(gpu, 16, 4, 64, 48, 16, "bfloat16", L, append=True)
+    announce("multi-query step", "L", L)
+    out, lse = g.decode_step_multi(x["q_nope"], x["q_rope"], x["M"], x["v_pool"],
+                                   x["k_pool"], x["block_table"], x["seq_lens"],
+                                   x["max_seq_len"], v_new=x["v_new"], k_new=x["k_new"],
+                                   rope_base=cfg.rope_base)
+    torch.cuda.synchronize()
+    vp, kp = o.append_tokens(h["v_pool"], h["k_pool"], h["v_new"], h["k_new"], h["pos"],
+                             h["block_table"], base=cfg.rope_base, cache_dtype="bfloat16")
+    for b, n in enumerate(MULTI_LENS):
+        for p in range(n - L, n):
+            blk, sl = int(h["block_table"][b, p // 64]), p % 64
+            np.testing.assert_array_equal(cpu(x["v_pool"][blk, sl]).double().numpy(),
+                                          vp[blk, sl])
+            np.testing.assert_array_equal(cpu(x["k_pool"][blk, sl]).double().numpy(),
+                                          kp[blk, sl])
+    ref, ref_lse = o.gva_decode_materialized_queries(
+        h["q_nope"], h["q_rope"], h["M"], vp, kp, h["block_table"], h["seq_lens"],
+        base=cfg.rope_base)
+    assert_bf16_parity(cpu(out).double().numpy(), ref)
+    np.testing.assert_allclose(cpu(lse).double().numpy(), ref_lse, rtol=0, atol=1e-3)
+
+
+def test_multi_query_one_token_is_the_single_query_call(g, gpu):
+    """q_len = 1 through the *_multi entry points gives the single-token
+    call's results bit for bit."""
+    cfg = syn.with_overrides(syn.get_config("decode_350m"), B=5, T=777)
+    x, h = gen(cfg, gpu)
+    announce("multi-query q_len 1")
+    qa1 = g.absorb_query(x["q_nope"], x["q_rope"], x["M"], x["pos"])
+    out1, lse1 = g.decode_attention(qa1, x["v_pool"], x["k_pool"], x["block_table"],
+                                    x["seq_lens"], x["max_seq_len"])
+    qam = g.absorb_query_multi(x["q_nope"][:, :, None].contiguous(),
+                               x["q_rope"][:, :, None].contiguous(), x["M"], x["pos"])
+    outm, lsem = g.decode_attention_multi(qam, x["v_pool"], x["k_pool"], x["block_table"],
+                                          x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    assert torch.equal(qam[:, :, 0], qa1)
+    assert torch.equal(outm[:, :, 0], out1)
+    assert torch.equal(lsem[:, :, 0], lse1)
+
+
+def test_multi_query_short_and_empty_sequences(g, gpu):
+    """0 < len < L is invalid (NaN for that sequence only); len = 0 gives
+    zeros and lse = -inf."""
+    L = 4
+    lens = [0, 3, 4, 70]
+    cfg, x, h = _multi_case(gpu, 16, 4, 64, 48, 16, "bfloat16", L, lens=lens)
+    announce("multi-query short sequences")
+    qa = g.absorb_query_multi(x["q_nope"], x["q_rope"], x["M"], x["pos"])
+    out, lse = g.decode_attention_multi(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                        x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    out, lse = cpu(out), cpu(lse)
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.all(torch.isnan(out[1]))
+    ref, _ = o.gva_decode_materialized_queries(
+        h["q_nope"], h["q_rope"], h["M"], h["v_pool"], h["k_pool"], h["block_table"],
+        h["seq_lens"], base=cfg.rope_base, seqs=[2, 3])
+    assert_bf16_parity(out[2:].double().numpy(), ref[2:])
+
+
+def test_multi_query_350m_shape_sampled(g, gpu):
+    """Four query tokens per sequence at the 350M decode shape (the launch
+    the benchmark times); the oracle checks three sequences in full."""
+    cfg = syn.get_config("decode_350m")
+    announce("multi-query 350M shape")
+    x = syn.make_gva_multi_inputs(cfg, 4, device=gpu)
+    qa = g.absorb_query_multi(x["q_nope"], x["q_rope"], x["M"], x["pos"])
+    out, lse = g.decode_attention_multi(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                        x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out))
+    for b in (0, 17, 31):
+        sub = seq_subpool(x, b)
+        ref, ref_lse = o.gva_decode_materialized_queries(
+            cpu(x["q_nope"][b:b + 1]), cpu(x["q_rope"][b:b + 1]), cpu(x["M"]),
+            sub["v_pool"], sub["k_pool"], sub["block_table"], sub["seq_lens"],
+            base=cfg.rope_base)
+        assert_bf16_parity(cpu(out[b:b + 1]).double().numpy(), ref, what=f"b={b}")
+        np.testing.assert_allclose(cpu(lse[b:b + 1]).double().numpy(), ref_lse, atol=1e-3)

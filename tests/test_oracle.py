@@ -457,3 +457,128 @@ def test_append_writes_rounded_rotated_token_in_paged_slot():
             else:
                 np.testing.assert_array_equal(vp2[blk, s], vp[blk, s])
                 np.testing.assert_array_equal(kp2[blk, s], kp[blk, s])
+
+
+# ------------------------------------------- several query tokens (L) ----
+
+def _queries(p, L, seed):
+    r = _rng(seed)
+    B, H = p["q_nope"].shape[:2]
+    return (r.standard_normal((B, H, L, p["d_n"])),
+            r.standard_normal((B, H, L, p["d_r"])))
+
+
+@pytest.mark.parametrize("L", [1, 2, 4])
+def test_queries_match_sdpa_with_causal_mask(L):
+    """L query tokens per sequence: torch SDPA (float64) over explicitly
+    built full keys, with a boolean mask letting query i (position T-L+i)
+    see positions 0..T-L+i only; RoPE written as complex multiplication."""
+    p = _problem(SHAPES[0], seed=30)
+    qn, qr = _queries(p, L, 31)
+    H, G, bs = p["H"], p["G"], p["block_size"]
+    scale = 1.0 / math.sqrt(p["d_n"] + p["d_r"])
+    out, lse = o.gva_decode_materialized_queries(
+        qn, qr, p["M"], p["v_pool"], p["k_pool"], p["block_table"],
+        p["seq_lens"], block_size=bs)
+    for b, n in enumerate(p["seq_lens"]):
+        rows = [(p["block_table"][b, j // bs], j % bs) for j in range(n)]
+        Vseq = np.stack([p["v_pool"][blk, s] for blk, s in rows])
+        kseq = np.stack([p["k_pool"][blk, s] for blk, s in rows])
+        allowed = np.arange(n)[None, :] <= (n - L + np.arange(L))[:, None]
+        for h in range(H):
+            g = h // (H // G)
+            K = np.concatenate([Vseq[:, g, :] @ p["M"][h], kseq], axis=1)
+            Q = np.stack([np.concatenate([qn[b, h, i],
+                                          _rope_complex(qr[b, h, i], n - L + i, 1e4)])
+                          for i in range(L)])
+            ref = F.scaled_dot_product_attention(
+                torch.from_numpy(Q)[None, None], torch.from_numpy(K)[None, None],
+                torch.from_numpy(np.ascontiguousarray(Vseq[:, g, :]))[None, None],
+                attn_mask=torch.from_numpy(allowed)[None, None], scale=scale)[0, 0].numpy()
+            np.testing.assert_allclose(out[b, h], ref, rtol=0, atol=1e-12)
+            s = scale * Q @ K.T
+            s[~allowed] = -np.inf
+            m = s.max(axis=1)
+            ref_lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+            np.testing.assert_allclose(lse[b, h], ref_lse, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("L", [2, 3])
+def test_query_token_i_is_single_query_decode_of_its_prefix(L):
+    """Query i equals the (separately pinned) single-query definition on the
+    first len-L+i+1 cached positions, with its own q slices."""
+    p = _problem(SHAPES[3], seed=32)
+    qn, qr = _queries(p, L, 33)
+    out, lse = o.gva_decode_materialized_queries(
+        qn, qr, p["M"], p["v_pool"], p["k_pool"], p["block_table"],
+        p["seq_lens"], block_size=p["block_size"])
+    for i in range(L):
+        o1, l1 = o.gva_decode_materialized(
+            qn[:, :, i], qr[:, :, i], p["M"], p["v_pool"], p["k_pool"],
+            p["block_table"], p["seq_lens"] - (L - 1) + i,
+            block_size=p["block_size"])
+        np.testing.assert_allclose(out[:, :, i], o1, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse[:, :, i], l1, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("L", [1, 3])
+def test_absorbed_queries_equal_materialized(L):
+    """Eq. 7 for several query tokens: absorbing each token's query and
+    attending over the value cache equals the materialised-key decode."""
+    p = _problem(SHAPES[2], seed=34)
+    qn, qr = _queries(p, L, 35)
+    out_m, lse_m = o.gva_decode_materialized_queries(
+        qn, qr, p["M"], p["v_pool"], p["k_pool"], p["block_table"],
+        p["seq_lens"], block_size=p["block_size"])
+    qa = o.absorb_queries(qn, qr, p["M"], p["seq_lens"] - 1)
+    out_a, lse_a = o.attend_absorbed_queries(
+        qa, p["v_pool"], p["k_pool"], p["block_table"], p["seq_lens"],
+        block_size=p["block_size"])
+    np.testing.assert_allclose(out_a, out_m, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse_a, lse_m, rtol=0, atol=1e-12)
+
+
+def test_absorb_queries_rows_are_single_token_absorptions():
+    r = _rng(36)
+    B, H, L, d_h, d_n, d_r = 3, 4, 3, 8, 6, 4
+    qn = r.standard_normal((B, H, L, d_n))
+    qr = r.standard_normal((B, H, L, d_r))
+    M = r.standard_normal((H, d_h, d_n))
+    pos_last = np.array([5, 2, 40])
+    qa = o.absorb_queries(qn, qr, M, pos_last, scale=0.3)
+    for i in range(L):
+        ref = o.absorb_query(qn[:, :, i], qr[:, :, i], M, pos_last - (L - 1) + i,
+                             scale=0.3)
+        np.testing.assert_allclose(qa[:, :, i], ref, rtol=0, atol=1e-14)
+    # the position slice of query i is rotated to its own position
+    np.testing.assert_allclose(
+        qa[1, 2, 0, d_h:], 0.3 * _rope_complex(qr[1, 2, 0], 0, 1e4), atol=1e-14)
+
+
+def test_append_tokens_write_each_token_at_its_position():
+    r = _rng(37)
+    B, L, G, d_h, d_r, bs = 2, 3, 2, 8, 4, 4
+    table = np.array([[3, 0, 5], [1, 4, 2]])
+    vp = r.standard_normal((6, bs, G, d_h))
+    kp = r.standard_normal((6, bs, d_r))
+    v_new = r.standard_normal((B, L, G, d_h))
+    k_new = r.standard_normal((B, L, d_r))
+    pos_last = np.array([5, 9])      # tokens at 3,4,5 and 7,8,9
+    vp2, kp2 = o.append_tokens(vp, kp, v_new, k_new, pos_last, table, base=1e4,
+                               block_size=bs, cache_dtype="float64")
+    written = {}
+    for b in range(B):
+        for i in range(L):
+            pp = pos_last[b] - (L - 1) + i
+            written[(table[b, pp // bs], pp % bs)] = (b, i, pp)
+    for blk in range(6):
+        for s in range(bs):
+            if (blk, s) in written:
+                b, i, pp = written[(blk, s)]
+                np.testing.assert_array_equal(vp2[blk, s], v_new[b, i])
+                np.testing.assert_allclose(kp2[blk, s],
+                                           _rope_complex(k_new[b, i], pp, 1e4),
+                                           atol=1e-14)
+            else:
+                np.testing.assert_array_equal(vp2[blk, s], vp[blk, s])
+                np.testing.assert_array_equal(kp2[blk, s], kp[blk, s])
