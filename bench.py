@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--workload", default="decode_350m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gqa", action="store_true")
+    ap.add_argument("--no-multi", action="store_true",
+                    help="skip the 4-query-token decode measurement")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--ingest-counters", nargs=4, metavar="DIR")
@@ -314,6 +316,16 @@ def main():
     if not args.no_gqa and cfg.cache_dtype == "bfloat16":
         extra["gqa"] = bench_gqa(torch, gva, syn, cfg0, dev, args.steps, args.warmup)
         extra["gqa"]["time_ratio_gva_over_gqa"] = dec_avg_ms * 1e3 / extra["gqa"]["us_avg"]
+    if not args.no_multi:
+        del pools
+        torch.cuda.empty_cache()
+        try:
+            extra["multi_query"] = bench_multi(torch, gva, syn, cfg0, dev, args.steps,
+                                               args.warmup, 4)
+            extra["multi_query"]["time_ratio_over_one_query"] = (
+                extra["multi_query"]["us_avg"] / (dec_avg_ms * 1e3))
+        except gva.GvaError as e:  # widths with no multi-query kernel
+            extra["multi_query"] = {"q_len": 4, "unsupported": str(e)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -354,6 +366,57 @@ def main():
         "extra": extra,
     }
     print(json.dumps(line))
+
+
+def bench_multi(torch, gva, syn, cfg, dev, steps, warmup, L):
+    """Decode of L query tokens per sequence (causal, the last L positions)
+    over the same caches, same rotation protocol: the cache is read once for
+    all L queries."""
+    y = syn.make_gva_multi_inputs(cfg, L, device=dev)
+    esize = 2 if cfg.cache_dtype == "bfloat16" else 4
+    tokens = int(y["seq_lens_host"].sum())
+    byts = tokens * (cfg.G * cfg.d_h + cfg.d_r) * esize
+    pool_bytes = (y["v_pool"].numel() + y["k_pool"].numel()) * esize
+    R = max(1, math.ceil(ROTATE_BYTES / pool_bytes))
+    pools = [(y["v_pool"], y["k_pool"])] + [
+        (y["v_pool"].clone(), y["k_pool"].clone()) for _ in range(R - 1)]
+    qa = gva.absorb_query_multi(y["q_nope"], y["q_rope"], y["M"], y["pos"],
+                                rope_base=cfg.rope_base)
+    ws = torch.zeros(max(16, gva.decode_workspace_bytes_multi(
+        cfg.B, cfg.H, L, y["v_pool"], y["k_pool"], y["block_table"], y["max_seq_len"])),
+        dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg.B, cfg.H, L, cfg.d_h), dtype=torch.float32, device=dev)
+    lse = torch.empty((cfg.B, cfg.H, L), dtype=torch.float32, device=dev)
+
+    def launch(i):
+        vp, kp = pools[i % R]
+        gva.decode_attention_multi(qa, vp, kp, y["block_table"], y["seq_lens"],
+                                   y["max_seq_len"], workspace=ws, out=out, lse=lse)
+
+    S = max(R, 8)
+    for i in range(max(warmup, S)):
+        launch(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(S):
+            launch(i)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, -(-steps // S))
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    avg = t0.elapsed_time(t1) / (reps * S)
+    del pools, y
+    torch.cuda.empty_cache()
+    return {"q_len": L, "us_avg": avg * 1e3, "cache_bytes": byts,
+            "GBps": byts / (avg * 1e-3) / 1e9,
+            "queries_ctx_per_s": L * tokens / (avg * 1e-3)}
 
 
 def bench_gqa(torch, gva, syn, cfg, dev, steps, warmup):
