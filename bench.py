@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--no-gqa", action="store_true")
     ap.add_argument("--no-multi", action="store_true",
                     help="skip the 4-query-token decode measurement")
+    ap.add_argument("--no-rope-keys", action="store_true",
+                    help="skip the rotated-reconstructed-key decode measurement")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--ingest-counters", nargs=4, metavar="DIR")
@@ -326,6 +328,11 @@ def main():
                 extra["multi_query"]["us_avg"] / (dec_avg_ms * 1e3))
         except gva.GvaError as e:  # widths with no multi-query kernel
             extra["multi_query"] = {"q_len": 4, "unsupported": str(e)}
+    if not args.no_rope_keys and cfg.cache_dtype == "bfloat16":
+        try:
+            extra["rope_on_keys"] = bench_rope_keys(torch, gva, syn, cfg0, dev, args.steps)
+        except gva.GvaError as e:
+            extra["rope_on_keys"] = {"unsupported": str(e)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -417,6 +424,65 @@ def bench_multi(torch, gva, syn, cfg, dev, steps, warmup, L):
     return {"q_len": L, "us_avg": avg * 1e3, "cache_bytes": byts,
             "GBps": byts / (avg * 1e-3) / 1e9,
             "queries_ctx_per_s": L * tokens / (avg * 1e-3)}
+
+
+def bench_rope_keys(torch, gva, syn, cfg, dev, steps):
+    """The variant with ordinary RoPE on the reconstructed key (no positional
+    slice, keys of width d_k = d_h) against the absorbed decode of the same
+    cache (d_r = 0, the same bytes): both timed with the same protocol."""
+    c0 = syn.with_overrides(cfg, d_n=cfg.d_h, d_r=0)
+    y = syn.make_gva_inputs(c0, device=dev)
+    tokens = int(y["seq_lens_host"].sum())
+    byts = tokens * c0.G * c0.d_h * 2
+    R = max(1, math.ceil(ROTATE_BYTES / (y["v_pool"].numel() * 2)))
+    pools = [y["v_pool"]] + [y["v_pool"].clone() for _ in range(R - 1)]
+    kp = y["k_pool"]
+    out = torch.empty((c0.B, c0.H, c0.d_h), dtype=torch.float32, device=dev)
+    lse = torch.empty((c0.B, c0.H), dtype=torch.float32, device=dev)
+    ws = torch.zeros(max(16, gva.decode_workspace_bytes(c0.B, c0.H, y["v_pool"], kp,
+                                                        y["block_table"], y["max_seq_len"])),
+                     dtype=torch.uint8, device=dev)
+    wsr = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+    qa = gva.absorb_query(y["q_nope"], y["q_rope"], y["M"], y["pos"])
+
+    def rope(i):
+        gva.decode_rope_keys(y["q_nope"], y["M"], pools[i % R], y["block_table"],
+                             y["seq_lens"], y["max_seq_len"], rope_base=c0.rope_base,
+                             workspace=wsr, out=out, lse=lse)
+
+    def absorbed(i):
+        gva.decode_attention(qa, pools[i % R], kp, y["block_table"], y["seq_lens"],
+                             y["max_seq_len"], workspace=ws, out=out, lse=lse)
+
+    res = {}
+    S = max(R, 8)
+    reps = max(1, -(-steps // S) // 4)
+    for name, fn in (("rope_on_keys", rope), ("absorbed", absorbed)):
+        for i in range(S):
+            fn(i)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(S):
+                fn(i)
+        gr.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            gr.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        res[name] = t0.elapsed_time(t1) / (reps * S) * 1e3
+        del gr
+    flops = 2.0 * tokens * c0.H * c0.d_h * c0.d_n
+    del pools, y
+    torch.cuda.empty_cache()
+    return {"d_k": c0.d_n, "cache_bytes": byts, "us_avg": res["rope_on_keys"],
+            "absorbed_us_avg_same_cache": res["absorbed"],
+            "time_ratio_over_absorbed": res["rope_on_keys"] / res["absorbed"],
+            "key_rebuild_TFLOPs": flops / (res["rope_on_keys"] * 1e-6) / 1e12}
 
 
 def bench_gqa(torch, gva, syn, cfg, dev, steps, warmup):

@@ -7,7 +7,7 @@ from . import _lib
 from ._lib import GvaError, GvaShape, LIB_PATH
 from .ops import (BLOCK_SIZE, absorb_query, absorb_query_multi, append_cache,
                   append_cache_multi, cache_scalars_per_token, decode_attention,
-                  decode_attention_multi, decode_step, decode_step_multi,
+                  decode_attention_multi, decode_rope_keys, decode_step, decode_step_multi,
                   decode_step_workspace_bytes, decode_workspace_bytes,
                   decode_workspace_bytes_multi, gqa_decode_attention,
                   gqa_decode_workspace_bytes, make_shape)
@@ -17,6 +17,7 @@ lib = _lib.load()
 __all__ = ["BLOCK_SIZE", "GvaError", "GvaShape", "LIB_PATH", "absorb_query",
            "absorb_query_multi", "append_cache", "append_cache_multi",
            "cache_scalars_per_token", "decode_attention", "decode_attention_multi",
+           "decode_rope_keys",
            "decode_step", "decode_step_multi", "decode_step_workspace_bytes",
            "decode_workspace_bytes", "decode_workspace_bytes_multi",
            "gqa_decode_attention", "gqa_decode_workspace_bytes", "lib", "make_shape"]

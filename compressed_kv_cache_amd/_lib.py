@@ -49,6 +49,9 @@ SIGNATURES = {
                                                     ctypes.POINTER(_SIZE)]),
     "gva_decode_step_multi": (_I32, [_SHAPE, _I32, _P, _P, _P, _F32, _F32, _P, _P, _P, _P, _P,
                                      _P, _I32, _P, _SIZE, _P, _P, _P]),
+    "gva_decode_rope_keys_workspace_size": (_I32, [_SHAPE, _I32, ctypes.POINTER(_SIZE)]),
+    "gva_decode_rope_keys": (_I32, [_SHAPE, _P, _P, _F32, _F32, _P, _P, _P, _I32, _P, _SIZE,
+                                    _P, _P, _P]),
     "gqa_decode_workspace_size": (_I32, [_SHAPE, _I32, ctypes.POINTER(_SIZE)]),
     "gqa_decode_attention": (_I32, [_SHAPE, _P, _F32, _P, _P, _P, _P, _I32, _P,
                                     _SIZE, _P, _P, _P]),

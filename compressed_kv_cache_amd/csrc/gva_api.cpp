@@ -15,6 +15,13 @@ bool mfma_decode_supported(const gva_shape& s, bool keys_separate, int q_len);
 DecodePlan plan_mfma_decode(const gva_shape& s, int max_seq_len, bool keys_separate);
 hipError_t launch_decode_mfma(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
                               hipStream_t stream);
+bool rope_keys_supported(const gva_shape& s);
+DecodePlan plan_rope_keys(const gva_shape& s, int max_seq_len);
+hipError_t launch_rope_keys(const gva_shape& s, const DecodePlan& plan, const float* q,
+                            const float* M, float q_scale, double base, const void* v_pool,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            int max_seq_len, float* partials, float* out, float* lse,
+                            hipStream_t stream);
 }  // namespace gva
 
 namespace {
@@ -374,6 +381,55 @@ gva_status gva_decode_step(const gva_shape* shape, const float* q_nope, const fl
   return gva_decode_step_multi(shape, 1, q_nope, q_rope, M, softmax_scale, rope_base, v_new,
                                k_new, v_pool, k_pool, block_table, seq_lens, max_seq_len,
                                workspace, workspace_bytes, out, lse, stream);
+}
+
+// Ordinary RoPE on the reconstructed key: d_n is the key width d_k, no
+// separate positional slice (d_r = 0).
+gva_status check_rope_keys(const gva_shape* shape, int32_t max_seq_len, float softmax_scale,
+                           float rope_base) {
+  if (!shape) return GVA_ERR_NULL;
+  gva_status st = check_cache_shape(*shape);
+  if (st != GVA_OK) return st;
+  if (shape->d_n < 2 || shape->d_n % 2 || shape->d_r != 0) return GVA_ERR_SHAPE;
+  if (!(rope_base > 0.f) || !isfinite(rope_base) || !isfinite(softmax_scale))
+    return GVA_ERR_SHAPE;
+  if (max_seq_len < 0 ||
+      static_cast<long long>(max_seq_len) >
+          static_cast<long long>(shape->max_blocks) * shape->block_size)
+    return GVA_ERR_SHAPE;
+  if (!gva::rope_keys_supported(*shape)) return GVA_ERR_UNSUPPORTED;
+  return GVA_OK;
+}
+
+gva_status gva_decode_rope_keys_workspace_size(const gva_shape* shape, int32_t max_seq_len,
+                                               size_t* bytes) {
+  if (!bytes) return GVA_ERR_NULL;
+  gva_status st = check_rope_keys(shape, max_seq_len, 0.f, 10000.f);
+  if (st != GVA_OK) return st;
+  *bytes = gva::plan_rope_keys(*shape, max_seq_len).workspace_bytes;
+  return GVA_OK;
+}
+
+gva_status gva_decode_rope_keys(const gva_shape* shape, const float* q, const float* M,
+                                float softmax_scale, float rope_base, const void* v_pool,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                                float* out, float* lse, void* stream) {
+  gva_status st = check_rope_keys(shape, max_seq_len, softmax_scale, rope_base);
+  if (st != GVA_OK) return st;
+  const gva_shape& s = *shape;
+  if (s.B == 0) return GVA_OK;
+  const gva::DecodePlan plan = gva::plan_rope_keys(s, max_seq_len);
+  if (!q || !M || !v_pool || !block_table || !seq_lens || !out || !workspace)
+    return GVA_ERR_NULL;
+  if (!aligned16(v_pool) || !aligned16(out) || !aligned16(workspace)) return GVA_ERR_ALIGN;
+  if (workspace_bytes < plan.workspace_bytes) return GVA_ERR_WORKSPACE;
+  const float scale =
+      softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(s.d_n));
+  return to_status(gva::launch_rope_keys(s, plan, q, M, scale, rope_base, v_pool, block_table,
+                                         seq_lens, max_seq_len,
+                                         static_cast<float*>(workspace), out, lse,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 gva_status gqa_decode_workspace_size(const gva_shape* shape, int32_t max_seq_len,

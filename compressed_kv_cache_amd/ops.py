@@ -407,3 +407,42 @@ def decode_step_multi(q_nope, q_rope, M, v_pool, k_pool, block_table, seq_lens, 
         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(dev))
     check("gva_decode_step_multi", st)
     return out, lse
+
+
+# ---- ordinary RoPE on the reconstructed key (no absorption) ----
+
+def decode_rope_keys(q, M, v_pool, block_table, seq_lens, max_seq_len, softmax_scale=None,
+                     rope_base=10000.0, workspace=None, out=None, lse=None, want_lse=True):
+    """out[B,H,d_h] (and lse[B,H]) of the variant whose keys R_j (v_j M_h)
+    are rebuilt and rotated per token (gva_decode_rope_keys); q[B,H,d_k]
+    unrotated, M[H,d_h,d_k]."""
+    dev = q.device
+    _need(q, "q", torch.float32, dev, 3)
+    _need(M, "M", torch.float32, dev, 3)
+    _need(v_pool, "v_pool", v_pool.dtype, dev, 4)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    B, H, d_k = q.shape
+    NB, bs, G, d_h = v_pool.shape
+    if tuple(M.shape) != (H, d_h, d_k) or block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("inconsistent shapes for decode_rope_keys")
+    s = GvaShape(B, H, G, d_h, d_k, 0, bs, block_table.shape[1], NB,
+                 _cache_dtype(v_pool, "v_pool"))
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    check("gva_decode_rope_keys_workspace_size", lib.gva_decode_rope_keys_workspace_size(
+        ctypes.byref(s), int(max_seq_len), ctypes.byref(n)))
+    if workspace is None:
+        workspace = torch.empty(max(n.value, 16), dtype=torch.uint8, device=dev)
+    if workspace.numel() * workspace.element_size() < n.value:
+        raise ValueError("workspace too small")
+    if out is None:
+        out = torch.empty((B, H, d_h), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    st = lib.gva_decode_rope_keys(
+        ctypes.byref(s), _ptr(q), _ptr(M), float(softmax_scale or 0.0), float(rope_base),
+        _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), int(max_seq_len), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(dev))
+    check("gva_decode_rope_keys", st)
+    return out, lse

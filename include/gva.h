@@ -253,6 +253,37 @@ gva_status gva_decode_step_multi(const gva_shape* shape, int32_t q_len,
                                  void* workspace, size_t workspace_bytes,
                                  float* out, float* lse, void* stream);
 
+/* Decode of the GVA variant that keeps ordinary RoPE on the whole
+ * reconstructed key (agihunt.info summary and cctest.ai article: the
+ * best-scoring GVA row, which cannot use absorbed decode):
+ *
+ *   k_j  = R(j) (V[b][j][g(h)] M_h)        (rebuilt and rotated per token)
+ *   score[b][h][j] = s * <R(t) q[b][h], k_j>,  t = seq_lens[b] - 1
+ *   p = softmax_j(score);   out[b][h] = sum_j p_j V[b][j][g(h)]
+ *
+ * R as in gva_absorb_query over all d_k = shape->d_n dims; the cache holds
+ * values only (d_r must be 0).  Because R(j) sits between the map and the
+ * query, M_h cannot be folded into the query once per step: every key is
+ * rebuilt at every step (d_h * d_k multiply-adds per token and head), which
+ * is the cost the decoupled slice avoids.
+ *   q [B][H][d_k] f32 (unrotated), M [H][d_h][d_k] f32, s = softmax_scale
+ *   or 1/sqrt(d_k) when <= 0; v_pool, block_table, seq_lens, max_seq_len,
+ *   out, lse as gva_decode_attention; workspace of at least
+ *   gva_decode_rope_keys_workspace_size bytes (16B; no zero-fill needed).
+ * Kernels exist for bf16 caches, d_h in {64, 128}, d_k in {16, 32, 48, 64},
+ * H/G <= 8; other sizes give GVA_ERR_UNSUPPORTED.  Two launches (partial
+ * records, then the log-sum-exp merge). */
+gva_status gva_decode_rope_keys_workspace_size(const gva_shape* shape,
+                                               int32_t max_seq_len,
+                                               size_t* bytes);
+gva_status gva_decode_rope_keys(const gva_shape* shape, const float* q,
+                                const float* M, float softmax_scale,
+                                float rope_base, const void* v_pool,
+                                const int32_t* block_table,
+                                const int32_t* seq_lens, int32_t max_seq_len,
+                                void* workspace, size_t workspace_bytes,
+                                float* out, float* lse, void* stream);
+
 /* Same-shape grouped-query attention decode, the baseline GVA is compared
  * with: each group stores both a key and a value row per token
  * (onedev.kr review, "What it is"; N_GQA = 2*T*G*d_h):

@@ -55,6 +55,7 @@ __all__ = [
     "attend_absorbed", "append_token", "gqa_decode", "chunk_partials",
     "merge_partials", "query_positions", "gva_decode_materialized_queries",
     "absorb_queries", "attend_absorbed_queries", "append_tokens",
+    "gva_decode_rope_on_keys",
 ]
 
 
@@ -470,6 +471,47 @@ def append_tokens(v_pool, k_pool, v_new, k_new, pos_last, block_table,
                                       base=base, block_size=block_size,
                                       cache_dtype=cache_dtype)
     return v_pool, k_pool
+
+
+# --------------------------------------------------------------------------
+# Ordinary RoPE on the reconstructed keys (the variant that cannot absorb)
+# --------------------------------------------------------------------------
+
+def gva_decode_rope_on_keys(q, M, v_pool, block_table, seq_lens, scale=None,
+                            base=10000.0, block_size=64, seqs=None, heads=None):
+    """GVA decode when ordinary RoPE acts on the whole reconstructed key.
+
+    q [B, H, d_k] (unrotated), M [H, d_h, d_k], cache = values only.  For
+    sequence b (query at position t = len_b - 1) and head h:
+      K_h[j] = R_j (V[b, j, g(h)] M_h)      (key rebuilt, then rotated at j)
+      q_r    = R_t q[b, h]
+      out, lse = softmax attention of q_r over K_h (scale 1/sqrt(d_k)),
+                 summing the values V[b, j, g(h)].
+    The rotation depends on j, so M_h cannot be folded into the query: every
+    key is rebuilt at every step (agihunt.info summary and cctest.ai article:
+    the best-scoring GVA row keeps ordinary RoPE on the reconstructed key and
+    cannot use absorbed decode).  Returns out [B, H, d_h], lse [B, H]."""
+    q, M = to_f64(q), to_f64(M)
+    v_pool = to_f64(v_pool)
+    block_table = np.asarray(block_table)
+    seq_lens = np.asarray(seq_lens).astype(np.int64)
+    B, H, d_k = q.shape
+    G, d_h = v_pool.shape[2], v_pool.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    out = np.full((B, H, d_h), np.nan)
+    lse = np.full((B, H), np.nan)
+    for b in _select(B, seqs):
+        n = int(seq_lens[b])
+        V_all = gather_tokens(v_pool, block_table[b], n, block_size)
+        for h in _select(H, heads):
+            g = head_group(h, H, G)
+            K = reconstruct_keys(V_all[:, g, :], M[h])            # [n, d_k]
+            K_rot = rope_rotate(K, np.arange(n), base)
+            q_r = rope_rotate(q[b, h], n - 1, base)
+            o, ls, _, _ = softmax_attention(q_r, K_rot, V_all[:, g, :], scale)
+            out[b, h], lse[b, h] = o, ls
+    return out, lse
 
 
 # --------------------------------------------------------------------------

@@ -253,3 +253,29 @@ def test_multi_entry_points_validate(g):
     _, need = _ws_multi(g, s, 4, 128)
     assert d(ctypes.byref(s), 4, P(0x10000), P(0x20000), P(0x30000), P(0x40000),
              P(0x50000), 128, P(0x60000), need - 1, P(0x70000), P(None), None) == 5
+
+
+# ---- ordinary RoPE on the reconstructed key ----
+
+def test_rope_keys_validation(g):
+    P = ctypes.c_void_p
+    n = ctypes.c_size_t(0)
+    f = g.lib.gva_decode_rope_keys_workspace_size
+    assert f(ctypes.byref(_shape(g, d_n=64, d_r=0)), 256, ctypes.byref(n)) == 0 and n.value > 0
+    assert f(ctypes.byref(_shape(g, d_n=64, d_r=16)), 256, ctypes.byref(n)) == 2  # no slice
+    assert f(ctypes.byref(_shape(g, d_n=63, d_r=0)), 256, ctypes.byref(n)) == 2   # odd width
+    assert f(ctypes.byref(_shape(g, d_n=40, d_r=0)), 256, ctypes.byref(n)) == 3   # no kernel
+    assert f(ctypes.byref(_shape(g, d_n=64, d_r=0)), 257, ctypes.byref(n)) == 2
+    d = g.lib.gva_decode_rope_keys
+    s = _shape(g, d_n=64, d_r=0)
+    args = [P(0x10000), P(0x20000), 0.0, 1e4, P(0x30000), P(0x40000), P(0x50000), 128,
+            P(0x60000), 1 << 30, P(0x70000), P(None), None]
+    bad = list(args)
+    bad[0] = P(None)
+    assert d(ctypes.byref(s), *bad) == 1
+    bad = list(args)
+    bad[3] = -1.0
+    assert d(ctypes.byref(s), *bad) == 2
+    bad = list(args)
+    bad[9] = 16
+    assert d(ctypes.byref(s), *bad) == 5

@@ -643,3 +643,66 @@ def test_multi_query_350m_shape_sampled(g, gpu):
             base=cfg.rope_base)
         assert_bf16_parity(cpu(out[b:b + 1]).double().numpy(), ref, what=f"b={b}")
         np.testing.assert_allclose(cpu(lse[b:b + 1]).double().numpy(), ref_lse, atol=1e-3)
+
+
+# ------------------------------ ordinary RoPE on the reconstructed key ----
+
+@pytest.mark.parametrize("H,G,d_h,d_k", [
+    (16, 4, 64, 64),
+    (16, 4, 64, 48),
+    (32, 8, 128, 64),
+    (8, 1, 64, 32),       # eight heads per group
+])
+def test_rope_on_keys_decode(g, gpu, H, G, d_h, d_k):
+    """Keys rebuilt and rotated per token, query rotated at len-1, against
+    the float64 oracle that forms every rotated key; ragged lengths."""
+    base = syn.get_config("long_ragged")
+    cfg = syn.with_overrides(base, B=len(EDGE_LENS), H=H, G=G, d_h=d_h, d_n=d_k, d_r=0,
+                             len_range=None, T=None)
+    lens = torch.tensor(EDGE_LENS, dtype=torch.int32)
+    x, h = gen(cfg, gpu, seq_lens=lens, shuffled=True)
+    announce("rope on keys", H, G, d_h, d_k)
+    out, lse = g.decode_rope_keys(x["q_nope"], x["M"], x["v_pool"], x["block_table"],
+                                  x["seq_lens"], x["max_seq_len"], rope_base=cfg.rope_base)
+    torch.cuda.synchronize()
+    ref, ref_lse = o.gva_decode_rope_on_keys(h["q_nope"], h["M"], h["v_pool"],
+                                             h["block_table"], h["seq_lens"],
+                                             base=cfg.rope_base)
+    assert_bf16_parity(cpu(out).double().numpy(), ref)
+    np.testing.assert_allclose(cpu(lse).double().numpy(), ref_lse, rtol=0, atol=1e-3)
+
+
+def test_rope_on_keys_350m_shape_sampled(g, gpu):
+    """The 350M decode shape without a positional slice (d_k = d_h = 64) at
+    full size; the oracle checks three sequences in full."""
+    cfg = syn.with_overrides(syn.get_config("decode_350m"), d_n=64, d_r=0)
+    announce("rope on keys 350M shape")
+    x = syn.make_gva_inputs(cfg, device=gpu)
+    out, lse = g.decode_rope_keys(x["q_nope"], x["M"], x["v_pool"], x["block_table"],
+                                  x["seq_lens"], x["max_seq_len"], rope_base=cfg.rope_base)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out))
+    for b in (0, 13, 31):
+        sub = seq_subpool(x, b, keys=("v_pool",))
+        ref, ref_lse = o.gva_decode_rope_on_keys(
+            cpu(x["q_nope"][b:b + 1]), cpu(x["M"]), sub["v_pool"], sub["block_table"],
+            sub["seq_lens"], base=cfg.rope_base)
+        assert_bf16_parity(cpu(out[b:b + 1]).double().numpy(), ref, what=f"b={b}")
+        np.testing.assert_allclose(cpu(lse[b:b + 1]).double().numpy(), ref_lse, atol=1e-3)
+
+
+def test_rope_on_keys_invalid_lengths(g, gpu):
+    """Zero length: zeros and -inf; a length past max_seq_len: NaN."""
+    cfg = syn.with_overrides(syn.get_config("decode_350m"), B=3, T=None, d_n=64, d_r=0,
+                             len_range=(1, 300))
+    lens = torch.tensor([0, 200, 150], dtype=torch.int32)
+    x, h = gen(cfg, gpu, seq_lens=lens)
+    x["seq_lens"][2] = 10 ** 6
+    announce("rope on keys invalid lengths")
+    out, lse = g.decode_rope_keys(x["q_nope"], x["M"], x["v_pool"], x["block_table"],
+                                  x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    out, lse = cpu(out), cpu(lse)
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.all(torch.isfinite(out[1]))
+    assert torch.all(torch.isnan(out[2]))

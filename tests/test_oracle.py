@@ -582,3 +582,68 @@ def test_append_tokens_write_each_token_at_its_position():
             else:
                 np.testing.assert_array_equal(vp2[blk, s], vp[blk, s])
                 np.testing.assert_array_equal(kp2[blk, s], kp[blk, s])
+
+
+# --------------------------- ordinary RoPE on the reconstructed key ----
+
+def test_rope_on_keys_matches_sdpa():
+    """Keys rebuilt as V_g M_h and rotated at their own positions (complex
+    multiplication), query rotated at len-1: torch SDPA in float64."""
+    p = _problem((8, 2, 16, 12, 2, 70), seed=40)
+    r = _rng(41)
+    B, H, G, bs = 2, 8, 2, p["block_size"]
+    q = r.standard_normal((B, H, 12))
+    out, lse = o.gva_decode_rope_on_keys(q, p["M"], p["v_pool"], p["block_table"],
+                                         p["seq_lens"], block_size=bs)
+    for b, n in enumerate(p["seq_lens"]):
+        rows = [(p["block_table"][b, j // bs], j % bs) for j in range(n)]
+        Vseq = np.stack([p["v_pool"][blk, s] for blk, s in rows])
+        for h in range(H):
+            g = h // (H // G)
+            K = np.stack([_rope_complex(Vseq[j, g] @ p["M"][h], j, 1e4) for j in range(n)])
+            qr = _rope_complex(q[b, h], n - 1, 1e4)
+            ref = _sdpa(qr, K, Vseq[:, g, :], 1.0 / math.sqrt(12))
+            np.testing.assert_allclose(out[b, h], ref, rtol=0, atol=1e-12)
+
+
+def test_rope_on_keys_depends_on_relative_positions_only():
+    """Shifting every cached position by p0 (keys rebuilt at p0 + j, query at
+    p0 + len - 1) leaves the output unchanged: R_t^T R_j = R_(j-t)."""
+    r = _rng(42)
+    H, G, d_h, d_k, T = 4, 2, 8, 6, 21
+    V = r.standard_normal((T, G, d_h))
+    M = r.standard_normal((H, d_h, d_k)) / math.sqrt(d_h)
+    q = r.standard_normal((1, H, d_k))
+    scale = 1.0 / math.sqrt(d_k)
+    base_out = None
+    for p0 in (0, 7, 1000, 100000):
+        outs = []
+        for h in range(H):
+            g = h // (H // G)
+            K = V[:, g] @ M[h]
+            Kr = _rope_complex(K, (p0 + np.arange(T))[:, None], 1e4)
+            qr = _rope_complex(q[0, h], p0 + T - 1, 1e4)
+            outs.append(o.softmax_attention(qr, Kr, V[:, g], scale)[0])
+        if base_out is None:
+            base_out = outs
+            vp, kp, table = _contiguous_pool(V, np.zeros((T, 2)), 8)
+            ref, _ = o.gva_decode_rope_on_keys(q, M, vp, table, [T], block_size=8)
+            np.testing.assert_allclose(ref[0], np.stack(outs), atol=1e-12)
+        else:
+            np.testing.assert_allclose(np.stack(outs), np.stack(base_out), atol=1e-9)
+
+
+def test_rope_on_keys_at_position_zero_is_plain_reconstructed_attention():
+    """A length-1 context (query and key at position 0, no rotation) is plain
+    attention with the reconstructed key: the output is the value itself."""
+    r = _rng(43)
+    V = r.standard_normal((1, 2, 8))
+    M = r.standard_normal((4, 8, 6))
+    q = r.standard_normal((1, 4, 6))
+    vp, _, table = _contiguous_pool(V, np.zeros((1, 2)), 4)
+    out, lse = o.gva_decode_rope_on_keys(q, M, vp, table, [1], block_size=4)
+    for h in range(4):
+        g = h // 2
+        np.testing.assert_allclose(out[0, h], V[0, g], atol=1e-15)
+        s = (q[0, h] @ (V[0, g] @ M[h])) / math.sqrt(6)
+        assert abs(lse[0, h] - s) < 1e-12
