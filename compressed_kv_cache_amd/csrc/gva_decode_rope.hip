@@ -41,6 +41,20 @@ constexpr int kMaxWaves = 8;   // heads per group handled by one block
 constexpr int kMaxPairs = 32;  // d_k <= 64
 constexpr float kLazyR = 8.0f;
 
+// Sum over the 16 lanes of a row (lanes 16r .. 16r+15) with DPP moves: two
+// quad permutations, then rotations by 4 and 8 within the row.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                              0xB1, 0xF, 0xF, false));  // xor 1
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                              0x4E, 0xF, 0xF, false));  // xor 2
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                              0x124, 0xF, 0xF, false));  // ror 4
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                              0x128, 0xF, 0xF, false));  // ror 8
+  return v;
+}
+
 // Rotation frequencies th_i / (2 pi) in float64 (revolutions per position).
 struct RevTable {
   double rev[kMaxPairs];
@@ -107,9 +121,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void rope_keys_kernel(
     for (int e = 0; e < 8; ++e) acc[s][e] = 0.f;
   int bad = 0;
 
-  // Tile loads run one tile ahead: the next tile's rows are requested
-  // before the current one is used (past the last tile the last one is
-  // read again, an in-bounds address whose registers are not used).
   auto tile_rows = [&](int j0, int& bad_out) -> size_t {
     int blk = bt[min(j0 / kBlockTok, max_blocks - 1)];
     if (blk < 0 || blk >= num_blocks) {
@@ -119,28 +130,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) void rope_keys_kernel(
     return static_cast<size_t>(blk) * kBlockTok + (j0 % kBlockTok) + li;
   };
   const int last_j0 = j_begin + ((j_end - j_begin - 1) / kTile) * kTile;
-  u32x4 nxt[KS];
-  {
-    const size_t row = tile_rows(j_begin, bad);
+  auto load_raw = [&](int j0, u32x4 (&dst)[KS]) {
+    const size_t row = tile_rows(min(j0, last_j0), bad);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      nxt[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + row * vrow + 32 * s));
-  }
-  for (int j0 = j_begin; j0 < j_end; j0 += kTile) {
+      dst[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + row * vrow + 32 * s));
+  };
+  // A operand of the tile at j0: token li, value dims 32s + 8q4 .. +7
+  // (rows past the end: 0)
+  auto operands = [&](int j0, const u32x4 (&raw)[KS], u32x4 (&dst)[KS]) {
     const int cnt = min(kTile, j_end - j0);
-    // A operand: token li, value dims 32s + 8q4 .. +7 (rows past the end: 0)
-    u32x4 av[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) av[s] = li < cnt ? nxt[s] : u32x4{0u, 0u, 0u, 0u};
-    {
-      const size_t row = tile_rows(min(j0 + kTile, last_j0), bad);
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        nxt[s] =
-            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + row * vrow + 32 * s));
-    }
-    // P[token 4q4 + r][column 16nt + li] = (v W)
-    f32x4 p4[NT];
+    for (int s = 0; s < KS; ++s) dst[s] = li < cnt ? raw[s] : u32x4{0u, 0u, 0u, 0u};
+  };
+  // P[token 4q4 + r][column 16nt + li] = (v W)
+  auto products = [&](const u32x4 (&av)[KS], f32x4 (&p4)[NT]) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       f32x4 a = {0.f, 0.f, 0.f, 0.f};
@@ -152,26 +156,31 @@ __global__ __launch_bounds__(64 * kMaxWaves) void rope_keys_kernel(
       }
       p4[nt] = a;
     }
-    // rotation weights: angle (j - t) th_i in revolutions, reduced in float64
+  };
+  // Rotation weights, score, online softmax and P.V of one tile whose
+  // products p4 and operands av are ready.
+  auto finish_tile = [&](int j0, const f32x4 (&p4)[NT], const u32x4 (&av)[KS]) {
+    const int cnt = min(kTile, j_end - j0);
+    // rotation weights: angle (j - t) th_i in revolutions, reduced in
+    // float64; even columns take the cosine, odd ones the sine, both as one
+    // hardware sine (the cosine a quarter turn ahead)
     float sc[4] = {0.f, 0.f, 0.f, 0.f};
+    const float quarter = (li & 1) ? 0.f : 0.25f;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const bool odd = li & 1;
       double r0 = static_cast<double>(j0 + 4 * q4 - t) * rev[nt];
       r0 -= rint(r0);
-      const float x0 = static_cast<float>(r0), step = static_cast<float>(rev[nt]);
+      const float x0 = static_cast<float>(r0) + quarter, step = static_cast<float>(rev[nt]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float x = fmaf(static_cast<float>(r), step, x0);
-        const float w = odd ? __builtin_amdgcn_sinf(x) : __builtin_amdgcn_cosf(x);
+        const float w = __builtin_amdgcn_sinf(fmaf(static_cast<float>(r), step, x0));
         sc[r] = fmaf(w, p4[nt][r], sc[r]);
       }
     }
     // sum over the 16 columns held by the lanes of one row group
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) sc[r] += __shfl_xor(sc[r], o, 64);
+      sc[r] = row16_sum(sc[r]);
       if (4 * q4 + r >= cnt) sc[r] = -INFINITY;
     }
     // online softmax over the tile (log2 units, lazy rescaling)
@@ -193,17 +202,31 @@ __global__ __launch_bounds__(64 * kMaxWaves) void rope_keys_kernel(
     l += (p[0] + p[1]) + (p[2] + p[3]);
     // P.V: lane (q4, li) adds p(token li) * v_li over its 8 dims per k-step;
     // token li's weight sits with the lanes of row group li/4, slot li%4
-    const int src = (li >> 2) * 16 + li;
-    const float g0 = __shfl(p[0], src, 64), g1 = __shfl(p[1], src, 64);
-    const float g2 = __shfl(p[2], src, 64), g3 = __shfl(p[3], src, 64);
+    // (every lane offers its own slot li%4, so one exchange serves all)
     const int rr = li & 3;
-    const float pv = rr == 0 ? g0 : rr == 1 ? g1 : rr == 2 ? g2 : g3;
+    const float offer = rr == 0 ? p[0] : rr == 1 ? p[1] : rr == 2 ? p[2] : p[3];
+    const float pv = __shfl(offer, (li >> 2) * 16 + li, 64);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const bf16x8 v8 = __builtin_bit_cast(bf16x8, av[s]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[s][e] = fmaf(pv, static_cast<float>(v8[e]), acc[s][e]);
     }
+  };
+
+  // Loads run one tile ahead: the next tile's rows are requested before
+  // this one's products (past the last tile the last one is read again, an
+  // in-bounds address whose registers are not used).  Running the products
+  // a tile ahead as well was measured slower (more registers per wave).
+  u32x4 raw[KS];
+  load_raw(j_begin, raw);
+  for (int j0 = j_begin; j0 < j_end; j0 += kTile) {
+    u32x4 av[KS];
+    f32x4 p4[NT];
+    operands(j0, raw, av);
+    load_raw(j0 + kTile, raw);
+    products(av, p4);
+    finish_tile(j0, p4, av);
   }
 
   // ---- one record per (chunk, head): [m, l, 0, 0, acc[0..DH)] ----
@@ -213,9 +236,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void rope_keys_kernel(
 #pragma unroll
   for (int s = 0; s < KS; ++s)
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) acc[s][e] += __shfl_xor(acc[s][e], o, 64);
+    for (int e = 0; e < 8; ++e) acc[s][e] = row16_sum(acc[s][e]);
   float* rec = part + ((static_cast<size_t>(b) * num_chunks + c) * H + h) * (DH + 4);
   if (li == 0) {
 #pragma unroll
@@ -252,11 +273,12 @@ bool rope_keys_supported(const gva_shape& s) {
   return d_k == 16 || d_k == 32 || d_k == 48 || d_k == 64;
 }
 
-// About 3 blocks per compute unit (the waves keep ~150 registers each).
+// About 4 blocks per compute unit over B*G*max_seq_len tokens (768-1536
+// measured within a few percent of each other at the 350M shape).
 DecodePlan plan_rope_keys(const gva_shape& s, int max_seq_len) {
   DecodePlan p{};
   p.kernel = kKernelRef;
-  const int target = env_target(768);
+  const int target = env_target(1024);
   const long long groups = static_cast<long long>(s.B) * s.G;
   const long long total = groups * (max_seq_len > 0 ? max_seq_len : 1);
   long long chunk = (total + target - 1) / target;
