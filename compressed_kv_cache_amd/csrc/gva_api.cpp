@@ -15,6 +15,11 @@ bool mfma_decode_supported(const gva_shape& s, bool keys_separate, int q_len);
 DecodePlan plan_mfma_decode(const gva_shape& s, int max_seq_len, bool keys_separate);
 hipError_t launch_decode_mfma(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
                               hipStream_t stream);
+bool prefill_supported(const gva_shape& s, int q_len);
+hipError_t launch_prefill(const gva_shape& s, int q_len, const float* qa, const void* v_pool,
+                          const void* k_pool, const int32_t* block_table,
+                          const int32_t* seq_lens, int max_seq_len, float* out, float* lse,
+                          hipStream_t stream);
 bool rope_keys_supported(const gva_shape& s);
 DecodePlan plan_rope_keys(const gva_shape& s, int max_seq_len);
 hipError_t launch_rope_keys(const gva_shape& s, const DecodePlan& plan, const float* q,
@@ -31,7 +36,10 @@ constexpr int kRefThreads = 256;
 constexpr int kRefAccMax = 32;
 constexpr size_t kRefSmemMax = 64 * 1024;
 constexpr int kTargetBlocks = 1024;  // split-chunk target for the reference kernel
-constexpr int kMaxQueryTokens = 64;  // query tokens per sequence in one call
+constexpr int kMaxQueryTokens = 65536;  // query tokens per sequence in one call
+// From this many query tokens per sequence on, the blocked kernel (queries
+// as matrix columns, key blocks staged once per block) takes the call.
+constexpr int kPrefillMinTokens = 16;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -116,17 +124,37 @@ gva_status ref_supported(const gva_shape& s, bool keys_separate) {
 }
 
 // Picks the kernel for a decode call (s: one column per head and query
-// token); fails when neither kernel covers it.
+// token); fails when no kernel covers it.
 gva_status make_plan(const gva_shape& s, int max_seq_len, bool keys_separate, int q_len,
                      gva::DecodePlan* plan) {
+  if (!keys_separate && q_len >= kPrefillMinTokens) {
+    gva_shape heads = s;  // the blocked kernel takes query heads, not columns
+    heads.H = s.H / q_len;
+    if (gva::prefill_supported(heads, q_len)) {
+      *plan = gva::DecodePlan{};
+      plan->kernel = gva::kKernelPrefill;
+      return GVA_OK;
+    }
+  }
   if (gva::mfma_decode_supported(s, keys_separate, q_len)) {
     *plan = gva::plan_mfma_decode(s, max_seq_len, keys_separate);
     return GVA_OK;
   }
   gva_status st = ref_supported(s, keys_separate);
-  if (st != GVA_OK) return st;
-  *plan = plan_ref(s, max_seq_len);
-  return GVA_OK;
+  if (st == GVA_OK) {
+    *plan = plan_ref(s, max_seq_len);
+    return GVA_OK;
+  }
+  if (!keys_separate) {  // a few query tokens the other kernels cannot take
+    gva_shape heads = s;
+    heads.H = s.H / q_len;
+    if (gva::prefill_supported(heads, q_len)) {
+      *plan = gva::DecodePlan{};
+      plan->kernel = gva::kKernelPrefill;
+      return GVA_OK;
+    }
+  }
+  return st;
 }
 
 gva_status check_decode_args(const gva_shape* shape, int32_t max_seq_len, bool keys_separate,
@@ -195,6 +223,9 @@ gva_status decode(const gva_shape* shape, int32_t q_len, const float* q, float q
   a.q_len = q_len;
   a.keys_separate = keys_separate;
   hipStream_t strm = static_cast<hipStream_t>(stream);
+  if (plan.kernel == gva::kKernelPrefill)
+    return to_status(gva::launch_prefill(*shape, q_len, q, v_pool, k_pool, block_table,
+                                         seq_lens, max_seq_len, out, lse, strm));
   if (plan.kernel == gva::kKernelMfma) return to_status(gva::launch_decode_mfma(s, plan, a, strm));
   return to_status(gva::launch_decode_ref(s, plan, a, strm));
 }
@@ -368,6 +399,9 @@ gva_status gva_decode_step_multi(const gva_shape* shape, int32_t q_len, const fl
   a.q_scale = 1.0f;
   a.q_len = q_len;
   a.keys_separate = false;
+  if (plan.kernel == gva::kKernelPrefill)
+    return to_status(gva::launch_prefill(s, q_len, qa, v_pool, k_pool, block_table, seq_lens,
+                                         max_seq_len, out, lse, strm));
   if (plan.kernel == gva::kKernelMfma) return to_status(gva::launch_decode_mfma(sc, plan, a, strm));
   return to_status(gva::launch_decode_ref(sc, plan, a, strm));
 }

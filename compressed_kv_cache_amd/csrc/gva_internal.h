@@ -27,7 +27,7 @@ struct DecodePlan {
 constexpr int kTicketStride = 64;  // u32 elements between counters
 inline size_t ticket_bytes(int B) { return static_cast<size_t>(B) * kTicketStride * 4; }
 
-enum { kKernelRef = 0, kKernelMfma = 1 };
+enum { kKernelRef = 0, kKernelMfma = 1, kKernelPrefill = 2 };
 
 DecodePlan plan_gva_decode(const gva_shape& s, int max_seq_len);
 DecodePlan plan_gqa_decode(const gva_shape& s, int max_seq_len);

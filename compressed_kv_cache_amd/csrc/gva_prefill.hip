@@ -1,0 +1,372 @@
+// Attention of many query tokens per sequence (prefill, or a long chunk of
+// new tokens after a cached prefix), absorbed form, on the gfx950 matrix
+// cores.  Query token i of L sits at position len - L + i and attends
+// causally; each query is absorbed on its own (qa = s*[q_nope M_h^T |
+// R(pos) q_rope]), so the keys are the cached values themselves plus the
+// shared positional key (onedev.kr review, "How it works" and "How it
+// differs").  The pages note that prefill is dominated by large matrix
+// products; here the products run on MFMA and the cache is read once per
+// block of queries, not once per query.
+//
+// Work split: block (query tile, sequence*G + g) owns 16*QW consecutive
+// query slots of the H/G heads of value group g (QW = 8 / (H/G)); its 8
+// waves each take 16 query slots of one head as the 16 MFMA columns.  The
+// block walks the key positions up to its last query in 64-token cache
+// blocks: the group's value rows and the positional key rows of a cache
+// block are staged once in LDS (double-buffered, the next block's loads in
+// flight meanwhile) and every wave reads its operands there:
+//   scores S^T[key][query] = V_g . qa^T (16x16x32) + k_rope . qr^T
+//   (16x16x16), qa split into bf16 high + low parts;
+//   online softmax per query column with the causal limit of that column;
+//   out^T += V_g^T P^T over 32 keys (16x16x32, V^T by the LDS transpose
+//   read, P split into bf16 high + low parts).
+// A wave whose queries all precede a key block skips its products there.
+// Query tiles are scheduled latest-first (they see the most keys).
+#include "gva_device.h"
+#include "gva_internal.h"
+
+namespace gva {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKeyBlock = 64;  // keys staged per step (one cache block)
+constexpr float kLazyP = 8.0f;
+
+__device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Value rows in LDS keep their 16-byte chunks XOR-permuted per row (within
+// the row's chunk count), so the row-wise operand reads and the transposed
+// P.V reads spread over the banks.
+template <int DH>
+__device__ __forceinline__ int vrow_off(int row, int chunk) {
+  constexpr int CH = DH / 8;  // 16-byte chunks per row
+  const int i = row & 15;
+  const int sw = (((i << 1) | (i >> 3)) & 15) & (CH - 1);
+  return row * (DH * 2) + ((chunk ^ sw) << 4);
+}
+
+template <int DH, int DR>
+struct PCfg {
+  static constexpr int KS = DH / 32;                  // 16x16x32 k-steps (values)
+  static constexpr int NR = DR > 0 ? (DR + 15) / 16 : 0;  // 16x16x16 k-steps (k_rope)
+  static constexpr int NRR = NR > 0 ? NR : 1;
+  static constexpr int DT = DH / 16;                  // 16-dim output tiles
+  static constexpr int VBYTES = kKeyBlock * DH * 2;   // staged value rows
+  static constexpr int KROW = DR > 0 ? DR * 2 : 16;   // staged k_rope row bytes
+  static constexpr int KBYTES = kKeyBlock * KROW;
+  static constexpr int BUF = VBYTES + KBYTES;
+  static constexpr int VLOADS = VBYTES / 16 / kThreads;        // 16-byte loads per thread
+  static constexpr int KLOADS = DR > 0 ? KBYTES / 16 : 0;       // threads with a k_rope load
+};
+
+template <int DH, int DR>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(
+    const float* __restrict__ qa, const bf16_t* __restrict__ v_pool,
+    const bf16_t* __restrict__ k_pool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, int max_seq_len, int H, int G, int L, int max_blocks,
+    int num_blocks, float* __restrict__ out, float* __restrict__ lse) {
+  using C = PCfg<DH, DR>;
+  constexpr int DQ = DH + DR;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * C::BUF];
+
+  const int hpg = H / G;
+  const int qw = kWaves / hpg;                        // 16-query sub-tiles per block
+  const int qt = gridDim.x - 1 - blockIdx.x;          // latest query tiles first
+  const int b = blockIdx.y / G, g = blockIdx.y % G;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q4 = lane >> 4, li = lane & 15;
+  const int h = g * hpg + wave % hpg;
+  const int slot0 = qt * 16 * qw + 16 * (wave / hpg);  // this wave's first query slot
+
+  int len = seq_lens[b];
+  const bool bad_len =
+      len < 0 || len > max_seq_len || len > max_blocks * kKeyBlock || (len > 0 && len < L);
+  if (bad_len || len == 0) {
+    // invalid: NaN; empty sequence: out = 0, lse = -inf
+    const float v = bad_len ? __builtin_nanf("") : 0.f;
+    const int slot = slot0 + li;
+    if (slot < L) {
+      float* o = out + ((static_cast<size_t>(b) * H + h) * L + slot) * DH;
+      for (int d = 4 * q4; d < DH; d += 16) *reinterpret_cast<float4*>(o + d) = float4{v, v, v, v};
+      if (lse && q4 == 0) lse[(static_cast<size_t>(b) * H + h) * L + slot] = bad_len ? v : -INFINITY;
+    }
+    return;
+  }
+
+  // query positions: slot i sits at len - L + i; the block sees keys up to
+  // its last query, the wave up to its own last one
+  const int base = len - L;
+  const int blk_last_slot = min(qt * 16 * qw + 16 * qw, L) - 1;
+  const int n_kb = (base + blk_last_slot) / kKeyBlock + 1;  // key blocks the block walks
+  const int my_slot = min(slot0 + li, L - 1);
+  const int my_pos = base + my_slot;                        // this lane's query position
+  const int wave_last = base + min(slot0 + 15, L - 1);      // last position in the wave
+
+  // ---- query operands (log2-scaled), bf16 hi + lo; lane li = query column ----
+  bf16x8 qh[C::KS], ql[C::KS];
+  s16x4 rh[C::NRR], rl[C::NRR];
+  {
+    const float* qrow = qa + ((static_cast<size_t>(b) * H + h) * L + my_slot) * DQ;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      const float4 x0 = *reinterpret_cast<const float4*>(qrow + 32 * s + 8 * q4);
+      const float4 x1 = *reinterpret_cast<const float4*>(qrow + 32 * s + 8 * q4 + 4);
+      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = kLog2e * x[e];
+        const __bf16 hi = static_cast<__bf16>(v);
+        qh[s][e] = hi;
+        ql[s][e] = static_cast<__bf16>(v - static_cast<float>(hi));
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < C::NRR; ++s) {
+      bf16x4 hh, ll;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 16 * s + 4 * q4 + e;
+        const float v = (d < DR) ? kLog2e * qrow[DH + d] : 0.f;
+        const __bf16 hi = static_cast<__bf16>(v);
+        hh[e] = hi;
+        ll[e] = static_cast<__bf16>(v - static_cast<float>(hi));
+      }
+      rh[s] = __builtin_bit_cast(s16x4, hh);
+      rl[s] = __builtin_bit_cast(s16x4, ll);
+    }
+  }
+
+  // ---- staging of one key block: value rows of group g, k_rope rows ----
+  const int32_t* bt = block_table + static_cast<size_t>(b) * max_blocks;
+  const size_t vrow = static_cast<size_t>(G) * DH;
+  u32x4 sv[C::VLOADS];
+  u32x4 sk = {0u, 0u, 0u, 0u};
+  int stage_bad = 0;
+  auto stage_load = [&](int kb) {
+    int blk = bt[min(kb, max_blocks - 1)];
+    if (blk < 0 || blk >= num_blocks) {
+      stage_bad = 1;
+      blk = 0;  // in the pool; the sequence is reported NaN
+    }
+    const size_t row0 = static_cast<size_t>(blk) * kKeyBlock;
+#pragma unroll
+    for (int x = 0; x < C::VLOADS; ++x) {
+      const int u = tid + kThreads * x;
+      const int r = u / (DH / 8), ch = u % (DH / 8);
+      sv[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          v_pool + (row0 + r) * vrow + static_cast<size_t>(g) * DH + 8 * ch));
+    }
+    if constexpr (DR > 0) {
+      if (tid < C::KLOADS) {
+        const int r = tid / (C::KROW / 16), ch = tid % (C::KROW / 16);
+        sk = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(k_pool + (row0 + r) * DR + 8 * ch));
+      }
+    }
+  };
+  // rows past the sequence end are staged as zeros (their slots may hold
+  // anything; their scores are masked and their values must add nothing)
+  auto stage_store = [&](int kb, int buf) {
+    unsigned char* base_p = lds + buf * C::BUF;
+#pragma unroll
+    for (int x = 0; x < C::VLOADS; ++x) {
+      const int u = tid + kThreads * x;
+      const int r = u / (DH / 8), ch = u % (DH / 8);
+      const bool live = kb * kKeyBlock + r < len;
+      *reinterpret_cast<u32x4*>(base_p + vrow_off<DH>(r, ch)) =
+          live ? sv[x] : u32x4{0u, 0u, 0u, 0u};
+    }
+    if constexpr (DR > 0) {
+      if (tid < C::KLOADS) {
+        const int r = tid / (C::KROW / 16), ch = tid % (C::KROW / 16);
+        const bool live = kb * kKeyBlock + r < len;
+        *reinterpret_cast<u32x4*>(base_p + C::VBYTES + r * C::KROW + 16 * ch) =
+            live ? sk : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
+  // ---- online softmax state of this lane's query column ----
+  float m = -INFINITY, l = 0.f;
+  f32x4 acc[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // scores of the 16 keys at rows r0 .. r0+15 of the staged block:
+  // S^T[key 4q4 + r][query li]
+  auto scores = [&](const unsigned char* bp, int r0) -> f32x4 {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      const bf16x8 op = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(bp + vrow_off<DH>(r0 + li, 4 * s + q4)));
+      a = mfma32(op, qh[s], a);
+      a = mfma32(op, ql[s], a);
+    }
+    // Scheduling fence: the value products of the tile issue before its
+    // positional products.  Without it the compiler's interleaving of the two
+    // score tiles for d_r = 24 gave wrong scores on gfx950 (every query row
+    // off, also with the positional inputs all zero); d_r = 16 and 32 were
+    // right either way.  The faulty instruction pattern was not isolated.
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (DR > 0) {
+#pragma unroll
+      for (int s = 0; s < C::NR; ++s) {
+        // lanes past d_r read an in-row address; their query entries are zero
+        const int d = min(16 * s + 4 * q4, DR - 4);
+        const s16x4 op = __builtin_bit_cast(
+            s16x4, *reinterpret_cast<const u32x2*>(bp + C::VBYTES + (r0 + li) * C::KROW + 2 * d));
+        a = mfma16(op, rh[s], a);
+        a = mfma16(op, rl[s], a);
+      }
+    }
+    return a;
+  };
+
+  // one pair of 16-key tiles (rows r0 .. r0+31, first key position j0)
+  auto pair = [&](const unsigned char* bp, int r0, int j0) {
+    const f32x4 sa = scores(bp, r0);
+    const f32x4 sb = scores(bp, r0 + 16);
+    float sv8[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv8[r] = (j0 + 4 * q4 + r <= my_pos) ? sa[r] : -INFINITY;
+      sv8[4 + r] = (j0 + 16 + 4 * q4 + r <= my_pos) ? sb[r] : -INFINITY;
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(sv8[0], sv8[1]), fmaxf(sv8[2], sv8[3])),
+                       fmaxf(fmaxf(sv8[4], sv8[5]), fmaxf(sv8[6], sv8[7])));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const bool raise = tmax > m + kLazyP;
+    if (__any(raise)) {
+      const float m_new = raise ? tmax : m;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) acc[dt] *= alpha;
+      m = m_new;
+    }
+    // a column that has seen no key yet keeps zero weights
+    const float mref = m == -INFINITY ? 0.f : m;
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sv8[e] - mref);
+    l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    bf16x8 ph, pl;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const __bf16 hi = static_cast<__bf16>(p[e]);
+      ph[e] = hi;
+      pl[e] = static_cast<__bf16>(p[e] - static_cast<float>(hi));
+    }
+    // out^T += V^T P^T: k-slot 8q4 + e is key 4q4 + e of the first tile
+    // (e < 4) or 4q4 + e - 4 of the second, in P and in the V^T operand
+    const int rr = li >> 2, c4 = li & 3;
+    const int rowA = r0 + 4 * q4 + rr, rowB = rowA + 16;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const int chunk = 2 * dt + (c4 >> 1);
+      const int within = 8 * (c4 & 1);
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(bp + vrow_off<DH>(rowA, chunk) + within));
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(bp + vrow_off<DH>(rowB, chunk) + within));
+      const bf16x8 vt = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[dt] = mfma32(vt, ph, acc[dt]);
+      acc[dt] = mfma32(vt, pl, acc[dt]);
+    }
+  };
+
+  // ---- walk the key blocks, double-buffered ----
+  stage_load(0);
+  stage_store(0, 0);
+  __syncthreads();
+  for (int kb = 0; kb < n_kb; ++kb) {
+    // next block's loads go out first (past the last block the last one is
+    // read again: an in-bounds address, never stored)
+    stage_load(min(kb + 1, n_kb - 1));
+    const unsigned char* bp = lds + (kb & 1) * C::BUF;
+    const int j0 = kb * kKeyBlock;
+    if (wave_last >= j0) {  // uniform over the wave
+      pair(bp, 0, j0);
+      pair(bp, 32, j0 + 32);
+    }
+    if (kb + 1 < n_kb) stage_store(kb + 1, (kb + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and store this lane's column ----
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  const int bad = __syncthreads_or(stage_bad);
+  const int slot = slot0 + li;
+  if (slot < L) {
+    const float inv = bad ? __builtin_nanf("") : 1.f / l;
+    float* o = out + ((static_cast<size_t>(b) * H + h) * L + slot) * DH;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+      *reinterpret_cast<float4*>(o + 16 * dt + 4 * q4) =
+          float4{acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv};
+    if (lse && q4 == 0)
+      lse[(static_cast<size_t>(b) * H + h) * L + slot] =
+          bad ? __builtin_nanf("") : kLn2 * (m + log2f(l));
+  }
+}
+
+}  // namespace
+
+bool prefill_supported(const gva_shape& s, int q_len) {
+  if (s.cache_dtype != GVA_BF16 || q_len < 1) return false;
+  if (s.H % s.G) return false;
+  const int hpg = s.H / s.G;
+  if (hpg != 1 && hpg != 2 && hpg != 4 && hpg != 8) return false;
+  if (s.d_h != 64 && s.d_h != 128) return false;
+  return s.d_r == 0 || s.d_r == 16 || s.d_r == 24 || s.d_r == 32;
+}
+
+// s.H counts query heads (not heads x tokens); out [B][H][L][d_h].
+hipError_t launch_prefill(const gva_shape& s, int q_len, const float* qa, const void* v_pool,
+                          const void* k_pool, const int32_t* block_table,
+                          const int32_t* seq_lens, int max_seq_len, float* out, float* lse,
+                          hipStream_t stream) {
+  if (!prefill_supported(s, q_len)) return hipErrorInvalidValue;
+  const int qw = kWaves / (s.H / s.G);
+  dim3 grid((q_len + 16 * qw - 1) / (16 * qw), s.B * s.G);
+#define GVA_PREFILL(DH, DR)                                                                    \
+  hipLaunchKernelGGL((prefill_kernel<DH, DR>), grid, dim3(kThreads), 0, stream, qa,            \
+                     static_cast<const bf16_t*>(v_pool), static_cast<const bf16_t*>(k_pool),   \
+                     block_table, seq_lens, max_seq_len, s.H, s.G, q_len, s.max_blocks,        \
+                     s.num_blocks, out, lse)
+  switch (s.d_h * 100 + s.d_r) {
+    case 6400: GVA_PREFILL(64, 0); break;
+    case 6416: GVA_PREFILL(64, 16); break;
+    case 6424: GVA_PREFILL(64, 24); break;
+    case 6432: GVA_PREFILL(64, 32); break;
+    case 12800: GVA_PREFILL(128, 0); break;
+    case 12816: GVA_PREFILL(128, 16); break;
+    case 12824: GVA_PREFILL(128, 24); break;
+    case 12832: GVA_PREFILL(128, 32); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef GVA_PREFILL
+  return hipGetLastError();
+}
+
+}  // namespace gva

@@ -199,7 +199,7 @@ gva_status gva_decode_step(const gva_shape* shape, const float* q_nope,
                            size_t workspace_bytes, float* out, float* lse,
                            void* stream);
 
-/* Several tokens per sequence (q_len = L, 1 <= L <= 64): the entry points
+/* Several tokens per sequence (q_len = L, 1 <= L <= 65536): the entry points
  * above with one more size.  Each query token is absorbed on its own, once
  * per head and token (onedev.kr review, "How it works"), and attends
  * causally; L = 1 is exactly the single-token call.  Layouts:
@@ -216,8 +216,16 @@ gva_status gva_decode_step(const gva_shape* shape, const float* q_nope,
  * gva_decode_step_multi: append the L new tokens (when v_new/k_new are
  *   given), absorb the L queries, decode; seq_lens already counts the new
  *   tokens.
+ * Kernels: with L >= 16, or where the split kernels have no instance for
+ *   the column count H*L, a bf16 cache with H/G in {1, 2, 4, 8}, d_h in
+ *   {64, 128} and d_r in {0, 16, 24, 32} goes to the blocked (prefill)
+ *   kernel: queries are matrix columns and each 64-token key block is
+ *   staged once per block of queries (the pages note that prefill is
+ *   dominated by large matrix products).  It needs no workspace
+ *   (gva_decode_workspace_bytes_multi may report 0).  Other L go to the
+ *   split decode kernels with H*L columns, or fail GVA_ERR_UNSUPPORTED.
  * Other arguments, errors and workspace rules as the single-token calls;
- * q_len < 1 is GVA_ERR_SHAPE, q_len > 64 GVA_ERR_UNSUPPORTED. */
+ * q_len < 1 is GVA_ERR_SHAPE, q_len > 65536 GVA_ERR_UNSUPPORTED. */
 gva_status gva_absorb_query_multi(const gva_shape* shape, int32_t q_len,
                                   const float* q_nope, const float* q_rope,
                                   const float* M, const int32_t* pos,

@@ -213,7 +213,8 @@ def test_multi_workspace_validates_q_len(g):
     s = _shape(g)
     assert _ws_multi(g, s, 0)[0] == 2
     assert _ws_multi(g, s, -3)[0] == 2
-    assert _ws_multi(g, s, 65)[0] == 3
+    assert _ws_multi(g, s, 65536)[0] == 0     # many query tokens: the blocked kernel
+    assert _ws_multi(g, s, 65537)[0] == 3
     st1, n1 = _ws_multi(g, s, 1)
     assert (st1, n1) == _ws(g, s)          # q_len = 1 is the single-token call
     st4, n4 = _ws_multi(g, s, 4)
@@ -279,3 +280,17 @@ def test_rope_keys_validation(g):
     bad = list(args)
     bad[9] = 16
     assert d(ctypes.byref(s), *bad) == 5
+
+
+def test_many_query_tokens_need_no_workspace(g):
+    """From 16 query tokens per sequence on, supported shapes go to the
+    blocked kernel, which keeps no split records."""
+    s = _shape(g)
+    assert _ws_multi(g, s, 16) == (0, 0)
+    assert _ws_multi(g, s, 256, 256) == (0, 0)
+    assert _ws_multi(g, s, 4)[1] > 0          # the split decode kernel
+    assert _ws_multi(g, s, 3)[0] == 0         # taken by some kernel
+    assert _ws_multi(g, s, 15)[0] == 0
+    f32 = _shape(g, cache_dtype=__import__("torch").float32)
+    st, n = _ws_multi(g, f32, 16)             # fp32 cache: the vector kernel
+    assert st in (0, 3)

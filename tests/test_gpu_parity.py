@@ -706,3 +706,101 @@ def test_rope_on_keys_invalid_lengths(g, gpu):
     assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
     assert torch.all(torch.isfinite(out[1]))
     assert torch.all(torch.isnan(out[2]))
+
+
+# --------------------------------- many query tokens (prefill kernel) ----
+
+@pytest.mark.parametrize("H,G,d_h,d_n,d_r,L,lens", [
+    (16, 4, 64, 48, 16, 100, [100, 101, 163, 640]),   # prefill and prefix + chunk
+    (16, 4, 64, 40, 24, 64, [64, 64, 65, 300]),
+    (32, 8, 128, 96, 32, 48, [48, 129, 200]),
+    (16, 4, 64, 64, 0, 33, [33, 97]),                  # no positional slice
+    (16, 2, 64, 48, 16, 40, [40, 77]),                 # eight heads per group
+    (8, 4, 64, 48, 16, 70, [70, 150]),                 # two heads per group
+    (4, 4, 128, 112, 16, 17, [17, 260]),               # one head per group
+    (16, 4, 64, 48, 16, 7, [7, 64, 90]),               # few tokens no other kernel takes
+    (8, 2, 128, 104, 24, 130, [130, 700]),             # d_h 128 with the 24-wide slice
+    (16, 4, 64, 48, 16, 333, [333, 900]),              # several query tiles, ragged tail
+])
+def test_many_query_tokens(g, gpu, H, G, d_h, d_n, d_r, L, lens):
+    """L query tokens per sequence through the blocked (prefill) kernel:
+    causal, after a cached prefix of len - L tokens, against the float64
+    oracle that materialises every key."""
+    cfg, x, h = _multi_case(gpu, H, G, d_h, d_n, d_r, "bfloat16", L, lens=lens)
+    announce("many query tokens", H, G, d_h, d_r, "L", L, lens)
+    qa = g.absorb_query_multi(x["q_nope"], x["q_rope"], x["M"], x["pos"],
+                              rope_base=cfg.rope_base)
+    out, lse = g.decode_attention_multi(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                        x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    ref, ref_lse = o.gva_decode_materialized_queries(
+        h["q_nope"], h["q_rope"], h["M"], h["v_pool"], h["k_pool"], h["block_table"],
+        h["seq_lens"], base=cfg.rope_base)
+    assert_bf16_parity(cpu(out).double().numpy(), ref)
+    np.testing.assert_allclose(cpu(lse).double().numpy(), ref_lse, rtol=0, atol=1e-3)
+
+
+def test_prefill_step_with_append(g, gpu):
+    """gva_decode_step_multi with 96 new tokens: all appended (values bit for
+    bit), then the causal attention of the 96 queries."""
+    L = 96
+    lens = [96, 200, 1000]
+    cfg, x, h = _multi_case(gpu, 16, 4, 64, 48, 16, "bfloat16", L, lens=lens, append=True)
+    announce("prefill step with append")
+    out, lse = g.decode_step_multi(x["q_nope"], x["q_rope"], x["M"], x["v_pool"],
+                                   x["k_pool"], x["block_table"], x["seq_lens"],
+                                   x["max_seq_len"], v_new=x["v_new"], k_new=x["k_new"],
+                                   rope_base=cfg.rope_base)
+    torch.cuda.synchronize()
+    vp, kp = o.append_tokens(h["v_pool"], h["k_pool"], h["v_new"], h["k_new"], h["pos"],
+                             h["block_table"], base=cfg.rope_base, cache_dtype="bfloat16")
+    for b, n in enumerate(lens):
+        for p in range(n - L, n):
+            blk, sl = int(h["block_table"][b, p // 64]), p % 64
+            np.testing.assert_array_equal(cpu(x["v_pool"][blk, sl]).double().numpy(),
+                                          vp[blk, sl])
+    ref, ref_lse = o.gva_decode_materialized_queries(
+        h["q_nope"], h["q_rope"], h["M"], vp, kp, h["block_table"], h["seq_lens"],
+        base=cfg.rope_base)
+    assert_bf16_parity(cpu(out).double().numpy(), ref)
+    np.testing.assert_allclose(cpu(lse).double().numpy(), ref_lse, rtol=0, atol=1e-3)
+
+
+def test_many_query_tokens_invalid_lengths(g, gpu):
+    """len = 0: zeros and -inf; 0 < len < L: NaN for that sequence only."""
+    L = 32
+    cfg, x, h = _multi_case(gpu, 16, 4, 64, 48, 16, "bfloat16", L, lens=[0, 20, 40])
+    announce("many query tokens, invalid lengths")
+    qa = g.absorb_query_multi(x["q_nope"], x["q_rope"], x["M"], x["pos"])
+    out, lse = g.decode_attention_multi(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                        x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    out, lse = cpu(out), cpu(lse)
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.all(torch.isnan(out[1]))
+    ref, _ = o.gva_decode_materialized_queries(
+        h["q_nope"], h["q_rope"], h["M"], h["v_pool"], h["k_pool"], h["block_table"],
+        h["seq_lens"], base=cfg.rope_base, seqs=[2])
+    assert_bf16_parity(out[2:].double().numpy(), ref[2:])
+
+
+def test_prefill_350m_shape_sampled(g, gpu):
+    """Prefill of 32 sequences of 4096 tokens at the 350M shape (every token a
+    query); the oracle checks two (sequence, head) pairs in full."""
+    cfg = syn.get_config("decode_350m")
+    L = cfg.T
+    announce("prefill 350M shape")
+    x = syn.make_gva_multi_inputs(cfg, L, device=gpu)
+    qa = g.absorb_query_multi(x["q_nope"], x["q_rope"], x["M"], x["pos"])
+    out, lse = g.decode_attention_multi(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                        x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out))
+    for b, hh in ((0, 0), (31, 13)):
+        sub = seq_subpool(x, b)
+        ref, ref_lse = o.gva_decode_materialized_queries(
+            cpu(x["q_nope"][b:b + 1]), cpu(x["q_rope"][b:b + 1]), cpu(x["M"]),
+            sub["v_pool"], sub["k_pool"], sub["block_table"], sub["seq_lens"],
+            base=cfg.rope_base, heads=[hh])
+        assert_bf16_parity(cpu(out[b, hh]).double().numpy(), ref[0, hh], what=f"b={b} h={hh}")
+        np.testing.assert_allclose(cpu(lse[b, hh]).double().numpy(), ref_lse[0, hh], atol=1e-3)
