@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = ("decode-attn cache GB/s (% of HBM peak) and queries*ctx/s, "
           "350M shape, T=4096")
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 ROTATE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["compressed_kv_cache_amd/csrc/gva_decode_mfma.hip",
@@ -69,6 +70,8 @@ def parse():
                     help="skip the 4-query-token decode measurement")
     ap.add_argument("--no-rope-keys", action="store_true",
                     help="skip the rotated-reconstructed-key decode measurement")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill leg (every query token of the context at once)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--ingest-counters", nargs=4, metavar="DIR")
@@ -334,6 +337,12 @@ def main():
         except gva.GvaError as e:
             extra["rope_on_keys"] = {"unsupported": str(e)}
 
+    if not args.no_prefill and cfg.cache_dtype == "bfloat16" and cfg.T and cfg.T <= 8192:
+        try:
+            extra["prefill"] = bench_prefill(torch, gva, syn, cfg0, dev)
+        except gva.GvaError as e:
+            extra["prefill"] = {"unsupported": str(e)}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg0, x, args.cpu_seconds)
@@ -424,6 +433,47 @@ def bench_multi(torch, gva, syn, cfg, dev, steps, warmup, L):
     return {"q_len": L, "us_avg": avg * 1e3, "cache_bytes": byts,
             "GBps": byts / (avg * 1e-3) / 1e9,
             "queries_ctx_per_s": L * tokens / (avg * 1e-3)}
+
+
+def bench_prefill(torch, gva, syn, cfg, dev, calls=10):
+    """Prefill: every position of each sequence is a query (L = T), causal,
+    through the blocked kernel.  Algorithmic work per (query, visible key)
+    pair is 2*(2*d_h + d_r) flops (score over d_h + d_r, P.V over d_h);
+    timed with HIP events on the launch stream around back-to-back calls."""
+    L = int(cfg.T)
+    y = syn.make_gva_multi_inputs(cfg, L, device=dev)
+    qa = gva.absorb_query_multi(y["q_nope"], y["q_rope"], y["M"], y["pos"],
+                                rope_base=cfg.rope_base)
+    out = torch.empty((cfg.B, cfg.H, L, cfg.d_h), dtype=torch.float32, device=dev)
+    lse = torch.empty((cfg.B, cfg.H, L), dtype=torch.float32, device=dev)
+
+    def launch():
+        gva.decode_attention_multi(qa, y["v_pool"], y["k_pool"], y["block_table"],
+                                   y["seq_lens"], y["max_seq_len"], out=out, lse=lse)
+
+    for _ in range(2):
+        launch()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(calls):
+        launch()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / calls
+    lens = [int(n) for n in y["seq_lens_host"].tolist()]
+    pairs = sum(sum(n - L + i + 1 for i in range(L)) for n in lens) * cfg.H
+    flops = 2.0 * pairs * (2 * cfg.d_h + cfg.d_r)
+    tflops = flops / (ms * 1e-3) / 1e12
+    del y, qa, out, lse
+    torch.cuda.empty_cache()
+    return {"q_len": L, "ms_avg": ms, "query_key_pairs": pairs,
+            "algorithmic_flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "kernel": "prefill_kernel"}}
 
 
 def bench_rope_keys(torch, gva, syn, cfg, dev, steps):

@@ -31,6 +31,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -117,6 +118,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   const int my_slot = min(slot0 + li, L - 1);
   const int my_pos = base + my_slot;                        // this lane's query position
   const int wave_last = base + min(slot0 + 15, L - 1);      // last position in the wave
+  const int wave_first = base + min(slot0, L - 1);          // first position in the wave
 
   // ---- query operands (log2-scaled), bf16 hi + lo; lane li = query column ----
   bf16x8 qh[C::KS], ql[C::KS];
@@ -208,10 +210,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // scores of the 16 keys at rows r0 .. r0+15 of the staged block:
-  // S^T[key 4q4 + r][query li]
-  auto scores = [&](const unsigned char* bp, int r0) -> f32x4 {
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+  // scores of the 16 keys at rows r0 .. r0+15 of the staged block, minus
+  // `shift` (the accumulators start there): S^T[key 4q4 + r][query li]
+  auto scores = [&](const unsigned char* bp, int r0, float shift) -> f32x4 {
+    f32x4 a = {shift, shift, shift, shift};
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
       const bf16x8 op = __builtin_bit_cast(
@@ -239,42 +241,70 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     return a;
   };
 
-  // one pair of 16-key tiles (rows r0 .. r0+31, first key position j0)
-  auto pair = [&](const unsigned char* bp, int r0, int j0) {
-    const f32x4 sa = scores(bp, r0);
-    const f32x4 sb = scores(bp, r0 + 16);
-    float sv8[8];
+  // maximum over the four lanes of a query column (lanes li + 16k)
+  auto col_max = [](float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  };
+
+  // one pair of 16-key tiles (rows r0 .. r0+31, first key position j0);
+  // `diag`: some key of the pair lies past some query of the wave
+  auto pair = [&](const unsigned char* bp, int r0, int j0, bool diag) {
+    // scores come out relative to the column's running maximum (0 before
+    // the column has one), so the exponentials need no subtraction
+    const float mref = m == -INFINITY ? 0.f : m;
+    const f32x4 sa = scores(bp, r0, -mref);
+    const f32x4 sb = scores(bp, r0 + 16, -mref);
+    float x[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sv8[r] = (j0 + 4 * q4 + r <= my_pos) ? sa[r] : -INFINITY;
-      sv8[4 + r] = (j0 + 16 + 4 * q4 + r <= my_pos) ? sb[r] : -INFINITY;
+      x[r] = sa[r];
+      x[4 + r] = sb[r];
     }
-    float tmax = fmaxf(fmaxf(fmaxf(sv8[0], sv8[1]), fmaxf(sv8[2], sv8[3])),
-                       fmaxf(fmaxf(sv8[4], sv8[5]), fmaxf(sv8[6], sv8[7])));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const bool raise = tmax > m + kLazyP;
-    if (__any(raise)) {
-      const float m_new = raise ? tmax : m;
+    if (diag) {  // uniform over the wave
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (j0 + 4 * q4 + r > my_pos) x[r] = -INFINITY;
+        if (j0 + 16 + 4 * q4 + r > my_pos) x[4 + r] = -INFINITY;
+      }
+    }
+    const float lmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    // a new maximum only when a score passes the current one by more than
+    // the lazy margin (or the column has none yet): rare after the first
+    // key block, so the column reduction sits behind a wave-uniform test
+    if (__any(lmax + mref > m + kLazyP)) {
+      const float tmax = col_max(lmax);
+      const bool raise = tmax + mref > m + kLazyP;  // same in a column's lanes
+      const float m_new = raise ? tmax + mref : m;
       const float alpha = raise ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+      const float back = raise ? mref - m_new : 0.f;
       l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) acc[dt] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] += back;
       m = m_new;
     }
-    // a column that has seen no key yet keeps zero weights
-    const float mref = m == -INFINITY ? 0.f : m;
     float p[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sv8[e] - mref);
+    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(x[e]);
     l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    bf16x8 ph, pl;
+    // P = high + low bf16 parts: the high part is p with its low 16 bits
+    // cleared (exact split), the low part the rounded remainder
+    u32x4 phw, plw;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const __bf16 hi = static_cast<__bf16>(p[e]);
-      ph[e] = hi;
-      pl[e] = static_cast<__bf16>(p[e] - static_cast<float>(hi));
+    for (int e = 0; e < 8; e += 2) {
+      const unsigned u0 = __float_as_uint(p[e]), u1 = __float_as_uint(p[e + 1]);
+      phw[e / 2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+      bf16x2 lo;
+      lo[0] = static_cast<__bf16>(p[e] - __uint_as_float(u0 & 0xffff0000u));
+      lo[1] = static_cast<__bf16>(p[e + 1] - __uint_as_float(u1 & 0xffff0000u));
+      plw[e / 2] = __builtin_bit_cast(unsigned, lo);
     }
+    const bf16x8 ph = __builtin_bit_cast(bf16x8, phw), pl = __builtin_bit_cast(bf16x8, plw);
     // out^T += V^T P^T: k-slot 8q4 + e is key 4q4 + e of the first tile
     // (e < 4) or 4q4 + e - 4 of the second, in P and in the V^T operand
     const int rr = li >> 2, c4 = li & 3;
@@ -305,8 +335,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const unsigned char* bp = lds + (kb & 1) * C::BUF;
     const int j0 = kb * kKeyBlock;
     if (wave_last >= j0) {  // uniform over the wave
-      pair(bp, 0, j0);
-      pair(bp, 32, j0 + 32);
+      pair(bp, 0, j0, j0 + 31 > wave_first);
+      pair(bp, 32, j0 + 32, j0 + 63 > wave_first);
     }
     if (kb + 1 < n_kb) stage_store(kb + 1, (kb + 1) & 1);
     __syncthreads();
