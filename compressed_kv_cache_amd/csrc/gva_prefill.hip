@@ -50,16 +50,36 @@ __device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// Value rows in LDS keep their 16-byte chunks XOR-permuted per row (within
-// the row's chunk count), so the row-wise operand reads and the transposed
-// P.V reads spread over the banks.
+// Value rows in LDS keep their 16-byte chunks XOR-permuted per row, so that
+// (a) the 16 rows one score-operand read touches (one chunk column) and
+// (b) the 8 rows x 2 chunks one transposed P.V read touches each fill the
+// banks without conflicts, whether a bank cycle serves 128 or 256 bytes.
+// At d_h = 64 (128-byte rows): even rows and odd rows each take all 8
+// permutations, rows 0-7 and 8-15 too, and (b) needs distinct perm >> 1 in
+// every 4 rows of a parity and in every 4 consecutive rows; the table
+// satisfies all of these.  At d_h = 128 the row parity is a fourth bit.
 template <int DH>
 __device__ __forceinline__ int vrow_off(int row, int chunk) {
-  constexpr int CH = DH / 8;  // 16-byte chunks per row
+  constexpr unsigned long long kPerm = 0x4602753157136420ull;  // row i -> nibble i
   const int i = row & 15;
-  const int sw = (((i << 1) | (i >> 3)) & 15) & (CH - 1);
+  int sw = static_cast<int>((kPerm >> (4 * i)) & 15u);
+  if constexpr (DH == 128) sw |= (i & 1) << 3;
   return row * (DH * 2) + ((chunk ^ sw) << 4);
 }
+
+// Slot of 8-byte piece p (4 positional dims) in staged k_rope row `row`:
+// p XOR a per-row fold, so the 16 rows one read instruction touches (4 or 8
+// pieces each) cover the banks without conflicts for 128- and 256-byte bank
+// cycles (32-byte rows: fold (row >> 2) & 3; 64-byte rows: (row >> 1) & 7).
+template <int KROW>
+__device__ __forceinline__ int rope_fold(int row) {
+  return KROW == 32 ? (row >> 2) & 3 : (row >> 1) & 7;
+}
+
+template <int N>
+struct BufTag {
+  static constexpr int value = N;
+};
 
 template <int DH, int DR>
 struct PCfg {
@@ -68,11 +88,14 @@ struct PCfg {
   static constexpr int NRR = NR > 0 ? NR : 1;
   static constexpr int DT = DH / 16;                  // 16-dim output tiles
   static constexpr int VBYTES = kKeyBlock * DH * 2;   // staged value rows
-  static constexpr int KROW = DR > 0 ? DR * 2 : 16;   // staged k_rope row bytes
+  // staged k_rope rows: 32 or 64 bytes (d_r = 24 padded to 64), in 8-byte
+  // pieces permuted per row (rope_piece)
+  static constexpr int KROW = DR == 0 ? 16 : DR <= 16 ? 32 : 64;
   static constexpr int KBYTES = kKeyBlock * KROW;
+  static constexpr int KIN = DR * 2 / 16;             // 16-byte loads per k_rope row
   static constexpr int BUF = VBYTES + KBYTES;
   static constexpr int VLOADS = VBYTES / 16 / kThreads;        // 16-byte loads per thread
-  static constexpr int KLOADS = DR > 0 ? KBYTES / 16 : 0;       // threads with a k_rope load
+  static constexpr int KLOADS = kKeyBlock * KIN;                // threads with a k_rope load
 };
 
 template <int DH, int DR>
@@ -176,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     }
     if constexpr (DR > 0) {
       if (tid < C::KLOADS) {
-        const int r = tid / (C::KROW / 16), ch = tid % (C::KROW / 16);
+        const int r = tid / C::KIN, ch = tid % C::KIN;
         sk = __builtin_nontemporal_load(
             reinterpret_cast<const u32x4*>(k_pool + (row0 + r) * DR + 8 * ch));
       }
@@ -196,10 +219,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     }
     if constexpr (DR > 0) {
       if (tid < C::KLOADS) {
-        const int r = tid / (C::KROW / 16), ch = tid % (C::KROW / 16);
+        const int r = tid / C::KIN, ch = tid % C::KIN;
         const bool live = kb * kKeyBlock + r < len;
-        *reinterpret_cast<u32x4*>(base_p + C::VBYTES + r * C::KROW + 16 * ch) =
-            live ? sk : u32x4{0u, 0u, 0u, 0u};
+        // pieces 2ch, 2ch+1 land in slots 2ch ^ f, 2ch+1 ^ f: one 16-byte
+        // pair, its halves swapped when f is odd
+        const int f = rope_fold<C::KROW>(r);
+        const u32x4 x = live ? sk : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(base_p + C::VBYTES + r * C::KROW + 8 * ((2 * ch) ^ (f & ~1))) =
+            (f & 1) ? u32x4{x[2], x[3], x[0], x[1]} : x;
       }
     }
   };
@@ -233,7 +260,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
         // lanes past d_r read an in-row address; their query entries are zero
         const int d = min(16 * s + 4 * q4, DR - 4);
         const s16x4 op = __builtin_bit_cast(
-            s16x4, *reinterpret_cast<const u32x2*>(bp + C::VBYTES + (r0 + li) * C::KROW + 2 * d));
+            s16x4, *reinterpret_cast<const u32x2*>(bp + C::VBYTES + (r0 + li) * C::KROW +
+                                                   8 * ((d >> 2) ^ rope_fold<C::KROW>(r0 + li))));
         a = mfma16(op, rh[s], a);
         a = mfma16(op, rl[s], a);
       }
@@ -328,18 +356,26 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   stage_load(0);
   stage_store(0, 0);
   __syncthreads();
-  for (int kb = 0; kb < n_kb; ++kb) {
+  // key block kb lives in buffer kb & 1; the loop runs two blocks per
+  // trip so that each buffer's address is a constant (LDS offsets fold into
+  // the instructions)
+  auto step = [&](int kb, auto buf_tag) {
+    constexpr int BI = decltype(buf_tag)::value;
     // next block's loads go out first (past the last block the last one is
     // read again: an in-bounds address, never stored)
     stage_load(min(kb + 1, n_kb - 1));
-    const unsigned char* bp = lds + (kb & 1) * C::BUF;
+    const unsigned char* bp = lds + BI * C::BUF;
     const int j0 = kb * kKeyBlock;
     if (wave_last >= j0) {  // uniform over the wave
       pair(bp, 0, j0, j0 + 31 > wave_first);
       pair(bp, 32, j0 + 32, j0 + 63 > wave_first);
     }
-    if (kb + 1 < n_kb) stage_store(kb + 1, (kb + 1) & 1);
+    if (kb + 1 < n_kb) stage_store(kb + 1, 1 - BI);
     __syncthreads();
+  };
+  for (int kb = 0; kb < n_kb; kb += 2) {
+    step(kb, BufTag<0>{});
+    if (kb + 1 < n_kb) step(kb + 1, BufTag<1>{});
   }
 
   // ---- normalise and store this lane's column ----
