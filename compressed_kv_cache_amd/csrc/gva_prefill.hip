@@ -232,10 +232,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   };
 
   // ---- online softmax state of this lane's query column ----
-  float m = -INFINITY, l = 0.f;
+  // m: the column's running maximum (log2 units); nm = -m once the column
+  // has one, else 0 (the scores are produced relative to it); lacc: the
+  // weight sums, every element the sum of the lane's column (taken on the
+  // matrix cores: a ones operand times P)
+  float m = -INFINITY, nm = 0.f;
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16x8 ones = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
 
   // scores of the 16 keys at rows r0 .. r0+15 of the staged block, minus
   // `shift` (the accumulators start there): S^T[key 4q4 + r][query li]
@@ -280,11 +286,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   // one pair of 16-key tiles (rows r0 .. r0+31, first key position j0);
   // `diag`: some key of the pair lies past some query of the wave
   auto pair = [&](const unsigned char* bp, int r0, int j0, bool diag) {
-    // scores come out relative to the column's running maximum (0 before
-    // the column has one), so the exponentials need no subtraction
-    const float mref = m == -INFINITY ? 0.f : m;
-    const f32x4 sa = scores(bp, r0, -mref);
-    const f32x4 sb = scores(bp, r0 + 16, -mref);
+    // scores come out relative to the column's running maximum (nm = -m),
+    // so the exponentials need no subtraction
+    const f32x4 sa = scores(bp, r0, nm);
+    const f32x4 sb = scores(bp, r0 + 16, nm);
     float x[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -298,28 +303,41 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
         if (j0 + 16 + 4 * q4 + r > my_pos) x[4 + r] = -INFINITY;
       }
     }
-    const float lmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    // a new maximum only when a score passes the current one by more than
-    // the lazy margin (or the column has none yet): rare after the first
-    // key block, so the column reduction sits behind a wave-uniform test
-    if (__any(lmax + mref > m + kLazyP)) {
-      const float tmax = col_max(lmax);
-      const bool raise = tmax + mref > m + kLazyP;  // same in a column's lanes
-      const float m_new = raise ? tmax + mref : m;
+    // A column needs a new maximum when a score passes the current one by
+    // more than the lazy margin, or has none yet.  Key 0 is visible to every
+    // query, so after the first pair every column has one and the test is
+    // "some x > kLazyP": on the float bits as signed integers that is exact
+    // for every non-NaN x (negative floats, -inf included, are negative
+    // integers; positive floats keep their order), and an integer maximum
+    // takes no canonicalising.
+    bool up = j0 == 0;
+    if (!up) {
+      int xi[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xi[e] = __float_as_int(x[e]);
+      const int imax = max(max(max(xi[0], xi[1]), max(xi[2], xi[3])),
+                           max(max(xi[4], xi[5]), max(xi[6], xi[7])));
+      up = __any(imax > __float_as_int(kLazyP));
+    }
+    if (up) {  // uniform over the wave; rare after the first key block
+      const float lmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                               fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      const float tmax = col_max(lmax);  // same in a column's four lanes
+      const bool raise = m == -INFINITY ? tmax > -INFINITY : tmax > kLazyP;
+      const float m_new = raise ? tmax - nm : m;
       const float alpha = raise ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
-      const float back = raise ? mref - m_new : 0.f;
-      l *= alpha;
+      const float back = raise ? -tmax : 0.f;  // x relative to m_new
+      lacc *= alpha;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) acc[dt] *= alpha;
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] += back;
       m = m_new;
+      nm = m == -INFINITY ? 0.f : -m;
     }
     float p[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(x[e]);
-    l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     // P = high + low bf16 parts: the high part is p with its low 16 bits
     // cleared (exact split), the low part the rounded remainder
     u32x4 phw, plw;
@@ -333,6 +351,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       plw[e / 2] = __builtin_bit_cast(unsigned, lo);
     }
     const bf16x8 ph = __builtin_bit_cast(bf16x8, phw), pl = __builtin_bit_cast(bf16x8, plw);
+    lacc = mfma32(ones, ph, lacc);
+    lacc = mfma32(ones, pl, lacc);
     // out^T += V^T P^T: k-slot 8q4 + e is key 4q4 + e of the first tile
     // (e < 4) or 4q4 + e - 4 of the second, in P and in the V^T operand
     const int rr = li >> 2, c4 = li & 3;
@@ -379,8 +399,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   }
 
   // ---- normalise and store this lane's column ----
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  const float l = lacc[0];
   const int bad = __syncthreads_or(stage_bad);
   const int slot = slot0 + li;
   if (slot < L) {
