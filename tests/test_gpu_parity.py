@@ -784,6 +784,51 @@ def test_many_query_tokens_invalid_lengths(g, gpu):
     assert_bf16_parity(out[2:].double().numpy(), ref[2:])
 
 
+def test_many_query_tokens_out_of_range_device_values(g, gpu):
+    """Blocked kernel: a block id past the pool or a length past max_seq_len
+    gives NaN rows for that sequence only."""
+    L = 40
+    cfg, x, h = _multi_case(gpu, 16, 4, 64, 48, 16, "bfloat16", L, lens=[100, 200, 150])
+    announce("many query tokens, out-of-range device values")
+    qa = g.absorb_query_multi(x["q_nope"], x["q_rope"], x["M"], x["pos"])
+    bt = x["block_table"].clone()
+    bt[1, 2] = x["num_blocks"] + 7
+    sl = x["seq_lens"].clone()
+    sl[2] = x["max_seq_len"] + 1
+    out, lse = g.decode_attention_multi(qa, x["v_pool"], x["k_pool"], bt, sl, x["max_seq_len"])
+    torch.cuda.synchronize()
+    out, lse = cpu(out), cpu(lse)
+    assert torch.isnan(out[1]).all() and torch.isnan(lse[1]).all()
+    assert torch.isnan(out[2]).all() and torch.isnan(lse[2]).all()
+    ref, _ = o.gva_decode_materialized_queries(
+        h["q_nope"], h["q_rope"], h["M"], h["v_pool"], h["k_pool"], h["block_table"],
+        h["seq_lens"], base=cfg.rope_base, seqs=[0])
+    assert_bf16_parity(out[:1].double().numpy(), ref[:1])
+
+
+def test_many_query_tokens_zero_query_is_running_mean(g, gpu):
+    """Closed form, no oracle: with qa = 0 every visible key weighs the same,
+    so query i (position len - L + i) returns the mean of the values at
+    positions 0 .. len - L + i of its group, and lse = ln(len - L + i + 1)."""
+    L = 200
+    cfg, x, h = _multi_case(gpu, 8, 2, 128, 112, 16, "bfloat16", L, lens=[200, 333])
+    announce("many query tokens, zero query")
+    qa = torch.zeros((cfg.B, cfg.H, L, cfg.d_h + cfg.d_r), device=gpu)
+    out, lse = g.decode_attention_multi(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                        x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    out, lse = cpu(out).double().numpy(), cpu(lse).double().numpy()
+    hpg = cfg.H // cfg.G
+    for b, n in enumerate([200, 333]):
+        V = o.gather_tokens(o.to_f64(h["v_pool"]), h["block_table"][b], n, cfg.block_size)
+        csum = np.cumsum(V, axis=0)  # [n, G, d_h]
+        pos = np.arange(n - L, n)
+        for hh in range(cfg.H):
+            ref = csum[pos, hh // hpg] / (pos + 1)[:, None]
+            assert_bf16_parity(out[b, hh], ref, what=f"b={b} h={hh}")
+            np.testing.assert_allclose(lse[b, hh], np.log(pos + 1.0), rtol=0, atol=1e-4)
+
+
 def test_prefill_350m_shape_sampled(g, gpu):
     """Prefill of 32 sequences of 4096 tokens at the 350M shape (every token a
     query); the oracle checks two (sequence, head) pairs in full."""
