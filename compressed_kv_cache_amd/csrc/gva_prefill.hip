@@ -15,8 +15,8 @@
 // blocks: the group's value rows and the positional key rows of a cache
 // block are staged once in LDS (double-buffered, the next block's loads in
 // flight meanwhile) and every wave reads its operands there:
-//   scores S^T[key][query] = V_g . qa^T (16x16x32) + k_rope . qr^T
-//   (16x16x16), qa split into bf16 high + low parts;
+//   scores S^T[key][query] = V_g . qa^T + k_rope . qr^T, all on
+//   16x16x32 products (qa split into bf16 high + low parts);
 //   online softmax per query column with the causal limit of that column;
 //   out^T += V_g^T P^T over 32 keys (16x16x32, V^T by the LDS transpose
 //   read, P split into bf16 high + low parts).
@@ -30,12 +30,10 @@ namespace gva {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kWaves = 8;
@@ -45,9 +43,6 @@ constexpr float kLazyP = 8.0f;
 
 __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 // Value rows in LDS keep their 16-byte chunks XOR-permuted per row, so that
@@ -67,13 +62,14 @@ __device__ __forceinline__ int vrow_off(int row, int chunk) {
   return row * (DH * 2) + ((chunk ^ sw) << 4);
 }
 
-// Slot of 8-byte piece p (4 positional dims) in staged k_rope row `row`:
-// p XOR a per-row fold, so the 16 rows one read instruction touches (4 or 8
-// pieces each) cover the banks without conflicts for 128- and 256-byte bank
-// cycles (32-byte rows: fold (row >> 2) & 3; 64-byte rows: (row >> 1) & 7).
+// Slot of 16-byte unit u (8 positional dims) in staged k_rope row `row`:
+// u XOR a per-row fold, so the 16 rows one read instruction touches cover
+// the banks without conflicts for 128- and 256-byte bank cycles (32-byte
+// rows: fold ((row >> 2) ^ (row >> 3)) & 1; 64-byte rows:
+// ((row >> 1) ^ (row >> 3)) & 3).
 template <int KROW>
 __device__ __forceinline__ int rope_fold(int row) {
-  return KROW == 32 ? (row >> 2) & 3 : (row >> 1) & 7;
+  return KROW == 32 ? ((row >> 2) ^ (row >> 3)) & 1 : ((row >> 1) ^ (row >> 3)) & 3;
 }
 
 template <int N>
@@ -84,12 +80,14 @@ struct BufTag {
 template <int DH, int DR>
 struct PCfg {
   static constexpr int KS = DH / 32;                  // 16x16x32 k-steps (values)
-  static constexpr int NR = DR > 0 ? (DR + 15) / 16 : 0;  // 16x16x16 k-steps (k_rope)
+  // positional k-steps: one 16x16x32 product per 16 dims, k-slots 0-15 the
+  // query's high part and 16-31 its low part against the same key dims
+  static constexpr int NR = DR > 0 ? (DR + 15) / 16 : 0;
   static constexpr int NRR = NR > 0 ? NR : 1;
   static constexpr int DT = DH / 16;                  // 16-dim output tiles
   static constexpr int VBYTES = kKeyBlock * DH * 2;   // staged value rows
-  // staged k_rope rows: 32 or 64 bytes (d_r = 24 padded to 64), in 8-byte
-  // pieces permuted per row (rope_piece)
+  // staged k_rope rows: 32 or 64 bytes (d_r = 24 padded to 64), in 16-byte
+  // units permuted per row (rope_fold)
   static constexpr int KROW = DR == 0 ? 16 : DR <= 16 ? 32 : 64;
   static constexpr int KBYTES = kKeyBlock * KROW;
   static constexpr int KIN = DR * 2 / 16;             // 16-byte loads per k_rope row
@@ -145,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 
   // ---- query operands (log2-scaled), bf16 hi + lo; lane li = query column ----
   bf16x8 qh[C::KS], ql[C::KS];
-  s16x4 rh[C::NRR], rl[C::NRR];
+  bf16x8 rq[C::NRR];  // positional k-step s: lanes q4 < 2 high parts, q4 >= 2 low parts
   {
     const float* qrow = qa + ((static_cast<size_t>(b) * H + h) * L + my_slot) * DQ;
 #pragma unroll
@@ -163,17 +161,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     }
 #pragma unroll
     for (int s = 0; s < C::NRR; ++s) {
-      bf16x4 hh, ll;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = 16 * s + 4 * q4 + e;
+      for (int e = 0; e < 8; ++e) {
+        const int d = 16 * s + 8 * (q4 & 1) + e;
         const float v = (d < DR) ? kLog2e * qrow[DH + d] : 0.f;
         const __bf16 hi = static_cast<__bf16>(v);
-        hh[e] = hi;
-        ll[e] = static_cast<__bf16>(v - static_cast<float>(hi));
+        rq[s][e] = q4 < 2 ? hi : static_cast<__bf16>(v - static_cast<float>(hi));
       }
-      rh[s] = __builtin_bit_cast(s16x4, hh);
-      rl[s] = __builtin_bit_cast(s16x4, ll);
     }
   }
 
@@ -221,12 +215,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       if (tid < C::KLOADS) {
         const int r = tid / C::KIN, ch = tid % C::KIN;
         const bool live = kb * kKeyBlock + r < len;
-        // pieces 2ch, 2ch+1 land in slots 2ch ^ f, 2ch+1 ^ f: one 16-byte
-        // pair, its halves swapped when f is odd
-        const int f = rope_fold<C::KROW>(r);
-        const u32x4 x = live ? sk : u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(base_p + C::VBYTES + r * C::KROW + 8 * ((2 * ch) ^ (f & ~1))) =
-            (f & 1) ? u32x4{x[2], x[3], x[0], x[1]} : x;
+        *reinterpret_cast<u32x4*>(base_p + C::VBYTES + r * C::KROW +
+                                  16 * (ch ^ rope_fold<C::KROW>(r))) =
+            live ? sk : u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -254,22 +245,20 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       a = mfma32(op, qh[s], a);
       a = mfma32(op, ql[s], a);
     }
-    // Scheduling fence: the value products of the tile issue before its
-    // positional products.  Without it the compiler's interleaving of the two
-    // score tiles for d_r = 24 gave wrong scores on gfx950 (every query row
-    // off, also with the positional inputs all zero); d_r = 16 and 32 were
-    // right either way.  The faulty instruction pattern was not isolated.
-    __builtin_amdgcn_sched_barrier(0);
     if constexpr (DR > 0) {
+      // same 16x16x32 shape as the value products, so the accumulator chain
+      // never switches shapes (a 16x16x16 product reading the result of a
+      // 16x16x32 one issued just before it, or the reverse, read a stale
+      // accumulator on gfx950); lanes q4 and q4 + 2 read the same 8 key
+      // dims, and where d_r = 24 leaves no fourth unit the lanes reread the
+      // third against zero query entries
 #pragma unroll
       for (int s = 0; s < C::NR; ++s) {
-        // lanes past d_r read an in-row address; their query entries are zero
-        const int d = min(16 * s + 4 * q4, DR - 4);
-        const s16x4 op = __builtin_bit_cast(
-            s16x4, *reinterpret_cast<const u32x2*>(bp + C::VBYTES + (r0 + li) * C::KROW +
-                                                   8 * ((d >> 2) ^ rope_fold<C::KROW>(r0 + li))));
-        a = mfma16(op, rh[s], a);
-        a = mfma16(op, rl[s], a);
+        const int u = min(2 * s + (q4 & 1), C::KIN - 1);
+        const bf16x8 op = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(bp + C::VBYTES + (r0 + li) * C::KROW +
+                                                    16 * (u ^ rope_fold<C::KROW>(r0 + li))));
+        a = mfma32(op, rq[s], a);
       }
     }
     return a;
