@@ -138,7 +138,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   const int n_kb = (base + blk_last_slot) / kKeyBlock + 1;  // key blocks the block walks
   const int my_slot = min(slot0 + li, L - 1);
   const int my_pos = base + my_slot;                        // this lane's query position
-  const int wave_last = base + min(slot0 + 15, L - 1);      // last position in the wave
+  // last position in the wave; a wave whose slots all lie past L (the last
+  // query tile of a short L) has no query and skips every product
+  const int wave_last = slot0 < L ? base + min(slot0 + 15, L - 1) : -1;
   const int wave_first = base + min(slot0, L - 1);          // first position in the wave
 
   // ---- query operands (log2-scaled), bf16 hi + lo; lane li = query column ----
