@@ -414,6 +414,8 @@ bool prefill_supported(const gva_shape& s, int q_len) {
   const int hpg = s.H / s.G;
   if (hpg != 1 && hpg != 2 && hpg != 4 && hpg != 8) return false;
   if (s.d_h != 64 && s.d_h != 128) return false;
+  // one grid row per (sequence, value group): within the grid's y limit
+  if (static_cast<long long>(s.B) * s.G > 65535) return false;
   return s.d_r == 0 || s.d_r == 16 || s.d_r == 24 || s.d_r == 32;
 }
 

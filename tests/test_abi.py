@@ -294,3 +294,14 @@ def test_many_query_tokens_need_no_workspace(g):
     f32 = _shape(g, cache_dtype=__import__("torch").float32)
     st, n = _ws_multi(g, f32, 16)             # fp32 cache: the vector kernel
     assert st in (0, 3)
+
+
+def test_many_query_tokens_grid_bound(g):
+    """The blocked kernel runs one grid row per (sequence, value group): a
+    batch past that bound goes to another kernel or is reported unsupported,
+    never launched out of range."""
+    ok = _shape(g, B=16383, G=4, H=16)      # 65532 rows
+    assert _ws_multi(g, ok, 64, 64) == (0, 0)
+    big = _shape(g, B=16384, G=4, H=16)     # 65536 rows
+    st, n = _ws_multi(g, big, 64, 64)
+    assert st == 3 or n > 0                  # not the blocked kernel
