@@ -37,6 +37,7 @@ constexpr int kRefAccMax = 32;
 constexpr size_t kRefSmemMax = 64 * 1024;
 constexpr int kTargetBlocks = 1024;  // split-chunk target for the reference kernel
 constexpr int kMaxQueryTokens = 65536;  // query tokens per sequence in one call
+constexpr int kMaxGridY = 65535;        // largest grid y dimension of a launch
 // From this many query tokens per sequence on, the blocked kernel (queries
 // as matrix columns, key blocks staged once per block) takes the call.
 constexpr int kPrefillMinTokens = 16;
@@ -53,6 +54,10 @@ gva_status check_cache_shape(const gva_shape& s) {
   if (s.max_blocks < 1 || s.num_blocks < 1) return GVA_ERR_SHAPE;
   if (s.cache_dtype != GVA_F32 && s.cache_dtype != GVA_BF16) return GVA_ERR_UNSUPPORTED;
   if (!dh_ok(s.d_h)) return GVA_ERR_UNSUPPORTED;
+  // the decode grids run one row per sequence (the rotated-key decode one
+  // per sequence and value group): within the grid's y limit
+  if (s.B > kMaxGridY || static_cast<long long>(s.B) * s.G > kMaxGridY)
+    return GVA_ERR_UNSUPPORTED;
   return GVA_OK;
 }
 

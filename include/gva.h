@@ -76,7 +76,9 @@ typedef enum gva_dtype {
 /* Sizes of one call.  Fields an entry point does not use are ignored.
  * Supported: 1 <= H/G, H % G == 0; d_h in {32, 64, 128} (GQA: d_h in
  * {32, 64, 128}); 0 <= d_r <= 64 and even; 1 <= d_n <= 256; block_size == 64;
- * num_blocks, max_blocks >= 1.  d_r = 0 drops the positional slice: then
+ * num_blocks, max_blocks >= 1; B * G <= 65535 for the entry points that
+ * read the caches (one launch row per sequence and value group; larger
+ * batches are GVA_ERR_UNSUPPORTED: split them).  d_r = 0 drops the positional slice: then
  * q_rope, k_new and k_pool are not read and may be NULL, and with M_h = I,
  * d_n = d_h it is the variant whose keys are the values themselves
  * (bisque.today explainer, Figure 3: half the GQA cache). */

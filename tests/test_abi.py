@@ -305,3 +305,10 @@ def test_many_query_tokens_grid_bound(g):
     big = _shape(g, B=16384, G=4, H=16)     # 65536 rows
     st, n = _ws_multi(g, big, 64, 64)
     assert st == 3 or n > 0                  # not the blocked kernel
+
+
+def test_batch_past_grid_bound_is_unsupported(g):
+    """B * G beyond the launch grid's y limit is refused up front."""
+    assert _ws(g, _shape(g, B=16383, G=4))[0] == 0
+    assert _ws(g, _shape(g, B=16384, G=4))[0] == 3
+    assert _ws(g, _shape(g, B=70000, G=1, H=4))[0] == 3
