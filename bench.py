@@ -466,10 +466,30 @@ def bench_prefill(torch, gva, syn, cfg, dev, calls=10):
     pairs = sum(sum(n - L + i + 1 for i in range(L)) for n in lens) * cfg.H
     flops = 2.0 * pairs * (2 * cfg.d_h + cfg.d_r)
     tflops = flops / (ms * 1e-3) / 1e12
-    del y, qa, out, lse
+    del y, qa
+    torch.cuda.empty_cache()
+    # the same-shape GQA prefill (keys and values cached per group, the
+    # comparison the pages draw for prefill), same protocol
+    z = syn.make_gqa_multi_inputs(cfg, L, device=dev)
+
+    def launch_gqa():
+        gva.gqa_decode_attention_multi(z["q"], z["k_pool"], z["v_pool"], z["block_table"],
+                                       z["seq_lens"], z["max_seq_len"], out=out, lse=lse)
+
+    for _ in range(2):
+        launch_gqa()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(calls):
+        launch_gqa()
+    t1.record()
+    torch.cuda.synchronize()
+    gqa_ms = t0.elapsed_time(t1) / calls
+    del z, out, lse
     torch.cuda.empty_cache()
     return {"q_len": L, "ms_avg": ms, "query_key_pairs": pairs,
             "algorithmic_flops": flops,
+            "gqa_ms_avg_same_shape": gqa_ms, "time_ratio_gva_over_gqa": ms / gqa_ms,
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / PEAK_BF16_TFLOPS, 4),

@@ -10,7 +10,7 @@ from .ops import (BLOCK_SIZE, absorb_query, absorb_query_multi, append_cache,
                   decode_attention_multi, decode_rope_keys, decode_step, decode_step_multi,
                   decode_step_workspace_bytes, decode_workspace_bytes,
                   decode_workspace_bytes_multi, gqa_decode_attention,
-                  gqa_decode_workspace_bytes, make_shape)
+                  gqa_decode_attention_multi, gqa_decode_workspace_bytes, make_shape)
 
 lib = _lib.load()
 
@@ -20,4 +20,5 @@ __all__ = ["BLOCK_SIZE", "GvaError", "GvaShape", "LIB_PATH", "absorb_query",
            "decode_rope_keys",
            "decode_step", "decode_step_multi", "decode_step_workspace_bytes",
            "decode_workspace_bytes", "decode_workspace_bytes_multi",
-           "gqa_decode_attention", "gqa_decode_workspace_bytes", "lib", "make_shape"]
+           "gqa_decode_attention", "gqa_decode_attention_multi", "gqa_decode_workspace_bytes",
+           "lib", "make_shape"]

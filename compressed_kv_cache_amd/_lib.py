@@ -55,6 +55,9 @@ SIGNATURES = {
     "gqa_decode_workspace_size": (_I32, [_SHAPE, _I32, ctypes.POINTER(_SIZE)]),
     "gqa_decode_attention": (_I32, [_SHAPE, _P, _F32, _P, _P, _P, _P, _I32, _P,
                                     _SIZE, _P, _P, _P]),
+    "gqa_decode_workspace_size_multi": (_I32, [_SHAPE, _I32, _I32, ctypes.POINTER(_SIZE)]),
+    "gqa_decode_attention_multi": (_I32, [_SHAPE, _I32, _P, _F32, _P, _P, _P, _P, _I32, _P,
+                                          _SIZE, _P, _P, _P]),
 }
 
 _lib = None

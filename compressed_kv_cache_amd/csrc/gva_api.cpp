@@ -15,11 +15,11 @@ bool mfma_decode_supported(const gva_shape& s, bool keys_separate, int q_len);
 DecodePlan plan_mfma_decode(const gva_shape& s, int max_seq_len, bool keys_separate);
 hipError_t launch_decode_mfma(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
                               hipStream_t stream);
-bool prefill_supported(const gva_shape& s, int q_len);
+bool prefill_supported(const gva_shape& s, int q_len, bool keys_separate);
 hipError_t launch_prefill(const gva_shape& s, int q_len, const float* qa, const void* v_pool,
                           const void* k_pool, const int32_t* block_table,
-                          const int32_t* seq_lens, int max_seq_len, float* out, float* lse,
-                          hipStream_t stream);
+                          const int32_t* seq_lens, int max_seq_len, bool keys_separate,
+                          float q_scale, float* out, float* lse, hipStream_t stream);
 bool rope_keys_supported(const gva_shape& s);
 DecodePlan plan_rope_keys(const gva_shape& s, int max_seq_len);
 hipError_t launch_rope_keys(const gva_shape& s, const DecodePlan& plan, const float* q,
@@ -132,10 +132,10 @@ gva_status ref_supported(const gva_shape& s, bool keys_separate) {
 // token); fails when no kernel covers it.
 gva_status make_plan(const gva_shape& s, int max_seq_len, bool keys_separate, int q_len,
                      gva::DecodePlan* plan) {
-  if (!keys_separate && q_len >= kPrefillMinTokens) {
+  if (q_len >= kPrefillMinTokens) {
     gva_shape heads = s;  // the blocked kernel takes query heads, not columns
     heads.H = s.H / q_len;
-    if (gva::prefill_supported(heads, q_len)) {
+    if (gva::prefill_supported(heads, q_len, keys_separate)) {
       *plan = gva::DecodePlan{};
       plan->kernel = gva::kKernelPrefill;
       return GVA_OK;
@@ -150,10 +150,10 @@ gva_status make_plan(const gva_shape& s, int max_seq_len, bool keys_separate, in
     *plan = plan_ref(s, max_seq_len);
     return GVA_OK;
   }
-  if (!keys_separate) {  // a few query tokens the other kernels cannot take
+  {  // a few query tokens the other kernels cannot take
     gva_shape heads = s;
     heads.H = s.H / q_len;
-    if (gva::prefill_supported(heads, q_len)) {
+    if (gva::prefill_supported(heads, q_len, keys_separate)) {
       *plan = gva::DecodePlan{};
       plan->kernel = gva::kKernelPrefill;
       return GVA_OK;
@@ -230,7 +230,8 @@ gva_status decode(const gva_shape* shape, int32_t q_len, const float* q, float q
   hipStream_t strm = static_cast<hipStream_t>(stream);
   if (plan.kernel == gva::kKernelPrefill)
     return to_status(gva::launch_prefill(*shape, q_len, q, v_pool, k_pool, block_table,
-                                         seq_lens, max_seq_len, out, lse, strm));
+                                         seq_lens, max_seq_len, keys_separate, q_scale, out,
+                                         lse, strm));
   if (plan.kernel == gva::kKernelMfma) return to_status(gva::launch_decode_mfma(s, plan, a, strm));
   return to_status(gva::launch_decode_ref(s, plan, a, strm));
 }
@@ -406,7 +407,7 @@ gva_status gva_decode_step_multi(const gva_shape* shape, int32_t q_len, const fl
   a.keys_separate = false;
   if (plan.kernel == gva::kKernelPrefill)
     return to_status(gva::launch_prefill(s, q_len, qa, v_pool, k_pool, block_table, seq_lens,
-                                         max_seq_len, out, lse, strm));
+                                         max_seq_len, false, 1.0f, out, lse, strm));
   if (plan.kernel == gva::kKernelMfma) return to_status(gva::launch_decode_mfma(sc, plan, a, strm));
   return to_status(gva::launch_decode_ref(sc, plan, a, strm));
 }
@@ -474,6 +475,25 @@ gva_status gva_decode_rope_keys(const gva_shape* shape, const float* q, const fl
 gva_status gqa_decode_workspace_size(const gva_shape* shape, int32_t max_seq_len,
                                      size_t* bytes) {
   return workspace_size(shape, max_seq_len, true, 1, bytes);
+}
+
+gva_status gqa_decode_workspace_size_multi(const gva_shape* shape, int32_t q_len,
+                                           int32_t max_seq_len, size_t* bytes) {
+  return workspace_size(shape, max_seq_len, true, q_len, bytes);
+}
+
+gva_status gqa_decode_attention_multi(const gva_shape* shape, int32_t q_len, const float* q,
+                                      float softmax_scale, const void* k_pool,
+                                      const void* v_pool, const int32_t* block_table,
+                                      const int32_t* seq_lens, int32_t max_seq_len,
+                                      void* workspace, size_t workspace_bytes, float* out,
+                                      float* lse, void* stream) {
+  if (!isfinite(softmax_scale)) return GVA_ERR_SHAPE;
+  float scale = softmax_scale;
+  if (shape && !(scale > 0.f) && shape->d_h > 0)
+    scale = 1.0f / sqrtf(static_cast<float>(shape->d_h));
+  return decode(shape, q_len, q, scale, k_pool, v_pool, block_table, seq_lens, max_seq_len,
+                workspace, workspace_bytes, out, lse, stream, true);
 }
 
 gva_status gqa_decode_attention(const gva_shape* shape, const float* q, float softmax_scale,

@@ -77,7 +77,7 @@ struct BufTag {
   static constexpr int value = N;
 };
 
-template <int DH, int DR>
+template <int DH, int DR, bool GQA>
 struct PCfg {
   static constexpr int KS = DH / 32;                  // 16x16x32 k-steps (values)
   // positional k-steps: one 16x16x32 product per 16 dims, k-slots 0-15 the
@@ -91,18 +91,26 @@ struct PCfg {
   static constexpr int KROW = DR == 0 ? 16 : DR <= 16 ? 32 : 64;
   static constexpr int KBYTES = kKeyBlock * KROW;
   static constexpr int KIN = DR * 2 / 16;             // 16-byte loads per k_rope row
-  static constexpr int BUF = VBYTES + KBYTES;
+  // GQA (keys cached per group, no positional slice): the group's key rows
+  // are staged after the value rows, in the same row layout
+  static constexpr int KOFF = VBYTES + KBYTES;
+  static constexpr int BUF = KOFF + (GQA ? VBYTES : 0);
   static constexpr int VLOADS = VBYTES / 16 / kThreads;        // 16-byte loads per thread
   static constexpr int KLOADS = kKeyBlock * KIN;                // threads with a k_rope load
 };
 
-template <int DH, int DR>
+// GQA = true is the same-shape grouped-query attention (the context the
+// pages compare against): qa is then the rotated query [B][H][L][d_h],
+// scaled by q_scale here, and k_pool the per-group key cache shaped like
+// v_pool; d_r is 0.
+template <int DH, int DR, bool GQA>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const float* __restrict__ qa, const bf16_t* __restrict__ v_pool,
     const bf16_t* __restrict__ k_pool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int max_seq_len, int H, int G, int L, int max_blocks,
-    int num_blocks, float* __restrict__ out, float* __restrict__ lse) {
-  using C = PCfg<DH, DR>;
+    int num_blocks, float q_scale, float* __restrict__ out, float* __restrict__ lse) {
+  static_assert(!GQA || DR == 0, "GQA has no positional slice");
+  using C = PCfg<DH, DR, GQA>;
   constexpr int DQ = DH + DR;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * C::BUF];
 
@@ -155,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = kLog2e * x[e];
+        const float v = kLog2e * q_scale * x[e];
         const __bf16 hi = static_cast<__bf16>(v);
         qh[s][e] = hi;
         ql[s][e] = static_cast<__bf16>(v - static_cast<float>(hi));
@@ -177,6 +185,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   const int32_t* bt = block_table + static_cast<size_t>(b) * max_blocks;
   const size_t vrow = static_cast<size_t>(G) * DH;
   u32x4 sv[C::VLOADS];
+  u32x4 skv[GQA ? C::VLOADS : 1];  // GQA key rows
   u32x4 sk = {0u, 0u, 0u, 0u};
   int stage_bad = 0;
   auto stage_load = [&](int kb) {
@@ -192,6 +201,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       const int r = u / (DH / 8), ch = u % (DH / 8);
       sv[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
           v_pool + (row0 + r) * vrow + static_cast<size_t>(g) * DH + 8 * ch));
+      if constexpr (GQA)
+        skv[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            k_pool + (row0 + r) * vrow + static_cast<size_t>(g) * DH + 8 * ch));
     }
     if constexpr (DR > 0) {
       if (tid < C::KLOADS) {
@@ -212,6 +224,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       const bool live = kb * kKeyBlock + r < len;
       *reinterpret_cast<u32x4*>(base_p + vrow_off<DH>(r, ch)) =
           live ? sv[x] : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (GQA)
+        *reinterpret_cast<u32x4*>(base_p + C::KOFF + vrow_off<DH>(r, ch)) =
+            live ? skv[x] : u32x4{0u, 0u, 0u, 0u};
     }
     if constexpr (DR > 0) {
       if (tid < C::KLOADS) {
@@ -242,8 +257,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     f32x4 a = {shift, shift, shift, shift};
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
+      // GVA scores against the value rows themselves, GQA against the keys
       const bf16x8 op = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(bp + vrow_off<DH>(r0 + li, 4 * s + q4)));
+          bf16x8, *reinterpret_cast<const u32x4*>(bp + (GQA ? C::KOFF : 0) +
+                                                  vrow_off<DH>(r0 + li, 4 * s + q4)));
       a = mfma32(op, qh[s], a);
       a = mfma32(op, ql[s], a);
     }
@@ -408,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 
 }  // namespace
 
-bool prefill_supported(const gva_shape& s, int q_len) {
+bool prefill_supported(const gva_shape& s, int q_len, bool keys_separate) {
   if (s.cache_dtype != GVA_BF16 || q_len < 1) return false;
   if (s.H % s.G) return false;
   const int hpg = s.H / s.G;
@@ -416,32 +433,44 @@ bool prefill_supported(const gva_shape& s, int q_len) {
   if (s.d_h != 64 && s.d_h != 128) return false;
   // one grid row per (sequence, value group): within the grid's y limit
   if (static_cast<long long>(s.B) * s.G > 65535) return false;
+  if (keys_separate) return true;  // GQA: no positional slice
   return s.d_r == 0 || s.d_r == 16 || s.d_r == 24 || s.d_r == 32;
 }
 
-// s.H counts query heads (not heads x tokens); out [B][H][L][d_h].
+// s.H counts query heads (not heads x tokens); out [B][H][L][d_h].  With
+// keys_separate the call is the GQA form (q rotated, scaled by q_scale;
+// k_pool shaped like v_pool); otherwise qa is absorbed and already scaled.
 hipError_t launch_prefill(const gva_shape& s, int q_len, const float* qa, const void* v_pool,
                           const void* k_pool, const int32_t* block_table,
-                          const int32_t* seq_lens, int max_seq_len, float* out, float* lse,
-                          hipStream_t stream) {
-  if (!prefill_supported(s, q_len)) return hipErrorInvalidValue;
+                          const int32_t* seq_lens, int max_seq_len, bool keys_separate,
+                          float q_scale, float* out, float* lse, hipStream_t stream) {
+  if (!prefill_supported(s, q_len, keys_separate)) return hipErrorInvalidValue;
   const int qw = kWaves / (s.H / s.G);
   dim3 grid((q_len + 16 * qw - 1) / (16 * qw), s.B * s.G);
-#define GVA_PREFILL(DH, DR)                                                                    \
-  hipLaunchKernelGGL((prefill_kernel<DH, DR>), grid, dim3(kThreads), 0, stream, qa,            \
+  const float scale = keys_separate ? q_scale : 1.f;
+#define GVA_PREFILL(DH, DR, GQ)                                                                \
+  hipLaunchKernelGGL((prefill_kernel<DH, DR, GQ>), grid, dim3(kThreads), 0, stream, qa,       \
                      static_cast<const bf16_t*>(v_pool), static_cast<const bf16_t*>(k_pool),   \
                      block_table, seq_lens, max_seq_len, s.H, s.G, q_len, s.max_blocks,        \
-                     s.num_blocks, out, lse)
-  switch (s.d_h * 100 + s.d_r) {
-    case 6400: GVA_PREFILL(64, 0); break;
-    case 6416: GVA_PREFILL(64, 16); break;
-    case 6424: GVA_PREFILL(64, 24); break;
-    case 6432: GVA_PREFILL(64, 32); break;
-    case 12800: GVA_PREFILL(128, 0); break;
-    case 12816: GVA_PREFILL(128, 16); break;
-    case 12824: GVA_PREFILL(128, 24); break;
-    case 12832: GVA_PREFILL(128, 32); break;
-    default: return hipErrorInvalidValue;
+                     s.num_blocks, scale, out, lse)
+  if (keys_separate) {
+    switch (s.d_h) {
+      case 64: GVA_PREFILL(64, 0, true); break;
+      case 128: GVA_PREFILL(128, 0, true); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (s.d_h * 100 + s.d_r) {
+      case 6400: GVA_PREFILL(64, 0, false); break;
+      case 6416: GVA_PREFILL(64, 16, false); break;
+      case 6424: GVA_PREFILL(64, 24, false); break;
+      case 6432: GVA_PREFILL(64, 32, false); break;
+      case 12800: GVA_PREFILL(128, 0, false); break;
+      case 12816: GVA_PREFILL(128, 16, false); break;
+      case 12824: GVA_PREFILL(128, 24, false); break;
+      case 12832: GVA_PREFILL(128, 32, false); break;
+      default: return hipErrorInvalidValue;
+    }
   }
 #undef GVA_PREFILL
   return hipGetLastError();

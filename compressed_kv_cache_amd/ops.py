@@ -409,6 +409,39 @@ def decode_step_multi(q_nope, q_rope, M, v_pool, k_pool, block_table, seq_lens, 
     return out, lse
 
 
+def gqa_decode_attention_multi(q, k_pool, v_pool, block_table, seq_lens, max_seq_len,
+                               softmax_scale=None, workspace=None, out=None, lse=None,
+                               want_lse=True):
+    """Same-shape GQA with L query tokens per sequence, query i at position
+    seq_lens-L+i attending causally (gqa_decode_attention_multi); q[B,H,L,d_h]
+    rotated."""
+    dev = q.device
+    _need(q, "q", torch.float32, dev, 4)
+    _need(v_pool, "v_pool", v_pool.dtype, dev, 4)
+    _need(k_pool, "k_pool", v_pool.dtype, dev, 4)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    B, H, L, d_h = q.shape
+    if tuple(k_pool.shape) != tuple(v_pool.shape) or v_pool.shape[3] != d_h:
+        raise ValueError("inconsistent shapes for gqa_decode_attention_multi")
+    s = _decode_shape(B, H, v_pool, 0, block_table, True)
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    check("gqa_decode_workspace_size_multi", lib.gqa_decode_workspace_size_multi(
+        ctypes.byref(s), L, int(max_seq_len), ctypes.byref(n)))
+    workspace = _workspace(n.value, dev, workspace)
+    if out is None:
+        out = torch.empty((B, H, L, d_h), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=dev)
+    st = lib.gqa_decode_attention_multi(
+        ctypes.byref(s), L, _ptr(q), float(softmax_scale or 0.0), _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_table), _ptr(seq_lens), int(max_seq_len), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(dev))
+    check("gqa_decode_attention_multi", st)
+    return out, lse
+
+
 # ---- ordinary RoPE on the reconstructed key (no absorption) ----
 
 def decode_rope_keys(q, M, v_pool, block_table, seq_lens, max_seq_len, softmax_scale=None,

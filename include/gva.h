@@ -306,6 +306,24 @@ gva_status gva_decode_rope_keys(const gva_shape* shape, const float* q,
  * Uses B, H, G, d_h, block_size, max_blocks, num_blocks, cache_dtype. */
 gva_status gqa_decode_workspace_size(const gva_shape* shape,
                                      int32_t max_seq_len, size_t* bytes);
+
+/* The same GQA context with q_len = L query tokens per sequence (query i at
+ * position seq_lens[b] - L + i, attending causally), the comparison the
+ * pages draw for prefill (onedev.kr review, "Premises and limits": prefill is
+ * dominated by matrix products, so GVA need not be faster there):
+ *   q [B][H][L][d_h] f32 (rotated), out [B][H][L][d_h], lse [B][H][L];
+ *   other arguments, errors and workspace rules as gqa_decode_attention and
+ *   the *_multi calls (L >= 16 on a bf16 cache with H/G in {1, 2, 4, 8},
+ *   d_h in {64, 128} takes the blocked kernel, no workspace). */
+gva_status gqa_decode_workspace_size_multi(const gva_shape* shape, int32_t q_len,
+                                           int32_t max_seq_len, size_t* bytes);
+gva_status gqa_decode_attention_multi(const gva_shape* shape, int32_t q_len,
+                                      const float* q, float softmax_scale,
+                                      const void* k_pool, const void* v_pool,
+                                      const int32_t* block_table,
+                                      const int32_t* seq_lens, int32_t max_seq_len,
+                                      void* workspace, size_t workspace_bytes,
+                                      float* out, float* lse, void* stream);
 gva_status gqa_decode_attention(const gva_shape* shape, const float* q,
                                 float softmax_scale, const void* k_pool,
                                 const void* v_pool,

@@ -55,7 +55,7 @@ __all__ = [
     "attend_absorbed", "append_token", "gqa_decode", "chunk_partials",
     "merge_partials", "query_positions", "gva_decode_materialized_queries",
     "absorb_queries", "attend_absorbed_queries", "append_tokens",
-    "gva_decode_rope_on_keys",
+    "gva_decode_rope_on_keys", "gqa_decode_queries",
 ]
 
 
@@ -408,6 +408,37 @@ def gva_decode_materialized_queries(q_nope, q_rope, M, v_pool, k_pool,
                 q_r = rope_rotate(q_rope[b, h, i], t, base)
                 query = np.concatenate([q_nope[b, h, i], q_r])
                 o, ls, _, _ = softmax_attention(query, keys[:t + 1],
+                                                V_all[:t + 1, g, :], scale)
+                out[b, h, i], lse[b, h, i] = o, ls
+    return out, lse
+
+
+def gqa_decode_queries(q, k_pool, v_pool, block_table, seq_lens, scale=None,
+                       block_size=64, seqs=None, heads=None):
+    """Grouped-query attention with L query tokens per sequence: the
+    comparison the pages draw for prefill ([review] "Premises and limits":
+    prefill is bound by matrix products, not by the cache).  q [B, H, L, d_h]
+    (already rotated); query token i of sequence b sits at position
+    t = len_b - L + i and sees positions 0..t of its group's key and value
+    streams.  Returns out [B, H, L, d_h], lse [B, H, L]."""
+    q = to_f64(q)
+    k_pool, v_pool = to_f64(k_pool), to_f64(v_pool)
+    block_table = np.asarray(block_table)
+    seq_lens = np.asarray(seq_lens).astype(np.int64)
+    B, H, L, d_h = q.shape
+    G = v_pool.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_h)
+    out = np.full((B, H, L, d_h), np.nan)
+    lse = np.full((B, H, L), np.nan)
+    for b in _select(B, seqs):
+        n = int(seq_lens[b])
+        K_all = gather_tokens(k_pool, block_table[b], n, block_size)
+        V_all = gather_tokens(v_pool, block_table[b], n, block_size)
+        for h in _select(H, heads):
+            g = head_group(h, H, G)
+            for i, t in enumerate(query_positions(n, L)):
+                o, ls, _, _ = softmax_attention(q[b, h, i], K_all[:t + 1, g, :],
                                                 V_all[:t + 1, g, :], scale)
                 out[b, h, i], lse[b, h, i] = o, ls
     return out, lse

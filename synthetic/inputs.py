@@ -36,7 +36,7 @@ from .configs import GVAConfig
 _STREAM = {
     "q_nope": 1, "q_rope": 2, "M": 3, "lens": 4, "perm": 5, "v_pool": 6,
     "k_pool": 7, "v_new": 8, "k_new": 9, "gqa_q": 10, "gqa_k": 11,
-    "mq_nope": 12, "mq_rope": 13, "mv_new": 14, "mk_new": 15,
+    "mq_nope": 12, "mq_rope": 13, "mv_new": 14, "mk_new": 15, "gqa_mq": 16,
 }
 
 _TORCH_DTYPE = {"float32": torch.float32, "bfloat16": torch.bfloat16}
@@ -219,6 +219,19 @@ def make_gqa_inputs(cfg: GVAConfig, device="cpu", seed: Optional[int] = None,
     out["block_table_host"] = table_cpu
     out["num_blocks"] = nb
     out["max_seq_len"] = max(lens) if lens else 0
+    return out
+
+
+def make_gqa_multi_inputs(cfg: GVAConfig, q_len: int, device="cpu",
+                          seed: Optional[int] = None,
+                          seq_lens: Optional[torch.Tensor] = None) -> Dict[str, object]:
+    """``make_gqa_inputs`` with ``q_len`` query tokens per sequence:
+    ``q[B,H,L,d_h]`` (rotated) for the last L positions of each sequence."""
+    out = make_gqa_inputs(cfg, device=device, seed=seed, seq_lens=seq_lens)
+    seed = out["seed"]
+    out["q_len"] = int(q_len)
+    out["q"] = _randn((cfg.B, cfg.H, int(q_len), cfg.d_h), torch.device(device), seed,
+                      "gqa_mq")
     return out
 
 

@@ -849,3 +849,42 @@ def test_prefill_350m_shape_sampled(g, gpu):
             base=cfg.rope_base, heads=[hh])
         assert_bf16_parity(cpu(out[b, hh]).double().numpy(), ref[0, hh], what=f"b={b} h={hh}")
         np.testing.assert_allclose(cpu(lse[b, hh]).double().numpy(), ref_lse[0, hh], atol=1e-3)
+
+
+# ------------------------------- same-shape GQA with many query tokens ----
+
+@pytest.mark.parametrize("H,G,d_h,L,lens", [
+    (16, 4, 64, 64, [64, 65, 300]),        # prefill and prefix + chunk
+    (32, 8, 128, 40, [40, 129]),           # d_h 128
+    (16, 2, 64, 17, [17, 90]),             # eight heads per group
+    (4, 4, 128, 100, [100, 230]),          # one head per group
+    (16, 4, 64, 5, [5, 70]),               # few tokens (vector or blocked kernel)
+])
+def test_gqa_many_query_tokens(g, gpu, H, G, d_h, L, lens):
+    """gqa_decode_attention_multi against the float64 GQA oracle: query i at
+    position len - L + i, causal, keys and values of its group."""
+    cfg = syn.with_overrides(syn.get_config("long_ragged"), B=len(lens), H=H, G=G, d_h=d_h,
+                             d_n=d_h, d_r=0, cache_dtype="bfloat16", len_range=None,
+                             T=None, append=False)
+    x = syn.make_gqa_multi_inputs(cfg, L, device=gpu,
+                                  seq_lens=torch.tensor(lens, dtype=torch.int32))
+    announce("gqa many query tokens", H, G, d_h, "L", L, lens)
+    out, lse = g.gqa_decode_attention_multi(x["q"], x["k_pool"], x["v_pool"],
+                                            x["block_table"], x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    ref, ref_lse = o.gqa_decode_queries(cpu(x["q"]), cpu(x["k_pool"]), cpu(x["v_pool"]),
+                                        cpu(x["block_table"]), cpu(x["seq_lens"]))
+    assert_bf16_parity(cpu(out).double().numpy(), ref)
+    np.testing.assert_allclose(cpu(lse).double().numpy(), ref_lse, rtol=0, atol=1e-3)
+
+
+def test_gqa_many_query_tokens_one_token_is_the_single_query_call(g, gpu):
+    cfg = syn.with_overrides(syn.get_config("decode_350m"), B=3, T=300)
+    x = syn.make_gqa_multi_inputs(cfg, 1, device=gpu)
+    announce("gqa many query tokens, L = 1")
+    o1, l1 = g.gqa_decode_attention_multi(x["q"], x["k_pool"], x["v_pool"], x["block_table"],
+                                          x["seq_lens"], x["max_seq_len"])
+    o0, l0 = g.gqa_decode_attention(x["q"][:, :, 0].contiguous(), x["k_pool"], x["v_pool"],
+                                    x["block_table"], x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, :, 0], o0) and torch.equal(l1[:, :, 0], l0)

@@ -647,3 +647,34 @@ def test_rope_on_keys_at_position_zero_is_plain_reconstructed_attention():
         np.testing.assert_allclose(out[0, h], V[0, g], atol=1e-15)
         s = (q[0, h] @ (V[0, g] @ M[h])) / math.sqrt(6)
         assert abs(lse[0, h] - s) < 1e-12
+
+
+@pytest.mark.parametrize("L", [1, 3, 8])
+def test_gqa_queries_match_sdpa_with_causal_mask(L):
+    """Many-token GQA oracle: torch SDPA (float64, enable_gqa) with a boolean
+    mask letting query i (position len-L+i) see positions 0..len-L+i only;
+    L = 1 is the single-query GQA oracle."""
+    r = _rng(40 + L)
+    B, H, G, d_h, bs = 2, 8, 2, 16, 8
+    lens = np.array([19, 11])
+    table = np.array([[2, 0, 3], [1, 4, 0]])
+    kp = r.standard_normal((5, bs, G, d_h))
+    vp = r.standard_normal((5, bs, G, d_h))
+    q = r.standard_normal((B, H, L, d_h))
+    out, lse = o.gqa_decode_queries(q, kp, vp, table, lens, block_size=bs)
+    for b in range(B):
+        n = int(lens[b])
+        j = np.arange(n)
+        Ks = kp[table[b, j // bs], j % bs]
+        Vs = vp[table[b, j // bs], j % bs]
+        allowed = j[None, :] <= (n - L + np.arange(L))[:, None]
+        kt = torch.from_numpy(np.ascontiguousarray(Ks.transpose(1, 0, 2)))[None]
+        vt = torch.from_numpy(np.ascontiguousarray(Vs.transpose(1, 0, 2)))[None]
+        ref = F.scaled_dot_product_attention(
+            torch.from_numpy(q[b])[None], kt, vt,
+            attn_mask=torch.from_numpy(allowed)[None, None], enable_gqa=True)
+        np.testing.assert_allclose(out[b], ref[0].numpy(), rtol=0, atol=1e-12)
+    if L == 1:
+        one, one_lse = o.gqa_decode(q[:, :, 0], kp, vp, table, lens, block_size=bs)
+        np.testing.assert_array_equal(out[:, :, 0], one)
+        np.testing.assert_array_equal(lse[:, :, 0], one_lse)
