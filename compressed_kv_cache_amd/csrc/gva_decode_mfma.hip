@@ -457,7 +457,7 @@ void decode_mfma_kernel(
     const float* __restrict__ q, const bf16_t* __restrict__ v_pool,
     const bf16_t* __restrict__ k_pool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int max_seq_len, int H, int G, int max_blocks,
-    int num_blocks, int chunk_tokens, int num_chunks, int q_len, float q_scale,
+    int num_blocks, int chunk_tokens, int num_chunks, int max_groups, int q_len, float q_scale,
     float* __restrict__ part,
     unsigned* __restrict__ tickets, float* __restrict__ out, float* __restrict__ lse) {
   using C = Cfg<GT, DH, DR, GQA>;
@@ -715,69 +715,108 @@ void decode_mfma_kernel(
   // ---- the last block of this sequence merges its chunk records ----
   // Records are written and read with device-scope accesses, which go to
   // the device coherence point instead of a CU-private cache line; the
-  // wait for outstanding stores orders them before the ticket.
+  // wait for outstanding stores orders them before the ticket.  A sequence
+  // of more than 2 kGroupChunks chunks merges in two levels (groups of
+  // kGroupChunks chunk records by each group's last block, then the group
+  // records by the last of those), so no single block reads more than
+  // max(kGroupChunks, groups) records; up to 2 kGroupChunks chunks one
+  // level is as fast (its rounds of loads cost about what the extra ticket
+  // and group round would).
   __shared__ int last_s;
   const int nc = (len + chunk_tokens - 1) / chunk_tokens;
+  const int ng = (max_groups > 0 && nc > 2 * kGroupChunks) ? (nc + kGroupChunks - 1) / kGroupChunks : 1;
+  const size_t rset = static_cast<size_t>(H) * C::REC;  // floats of one record set
+  unsigned* seq_ticket = tickets + static_cast<size_t>(b) * (1 + max_groups) * kTicketStride;
+  float* groups = part + static_cast<size_t>(gridDim.y) * num_chunks * rset;
+  // whether this block drew the last of n tickets (every thread sees it)
+  auto last_of = [&](unsigned* t, int n) -> bool {
+    if (threadIdx.x == 0)
+      last_s = __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               static_cast<unsigned>(n - 1);
+    __syncthreads();
+    return last_s != 0;
+  };
+  // Combines `count` record sets at src (consecutive) into out/lse, or, with
+  // dst, into one record set.  Each thread takes one head and 4 output dims,
+  // U records per round: the loads of a round are independent and overlap
+  // in flight, and rounds are combined online (log-sum-exp).  A record
+  // whose maximum is -inf (no token seen) weighs 0.
+  auto merge = [&](const float* src, int count, float* dst) {
+    for (int i = threadIdx.x; i < H * (DH / 4); i += kThreads) {
+      const int hh = i / (DH / 4);
+      const int d4 = (i % (DH / 4)) * 4;
+      const float* r0 = src + hh * C::REC;
+      float m_run = -INFINITY, L = 0.f;
+      float4 o = {0.f, 0.f, 0.f, 0.f};
+      constexpr int U = 8;
+      for (int c0 = 0; c0 < count; c0 += U) {
+        float2 ml[U], a[U], bb[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {  // past the last record: reload it, weight 0
+          const float* r = r0 + min(c0 + u, count - 1) * rset;
+          ml[u] = load_dev2(r);
+          a[u] = load_dev2(r + 4 + d4);
+          bb[u] = load_dev2(r + 6 + d4);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (c0 + u >= count) ml[u] = float2{-INFINITY, 0.f};
+        float m_new = m_run;
+#pragma unroll
+        for (int u = 0; u < U; ++u) m_new = fmaxf(m_new, ml[u].x);
+        const float sc = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        L *= sc;
+        o.x *= sc;
+        o.y *= sc;
+        o.z *= sc;
+        o.w *= sc;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float wt =
+              ml[u].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[u].x - m_new);
+          L = fmaf(wt, ml[u].y, L);
+          o.x = fmaf(wt, a[u].x, o.x);
+          o.y = fmaf(wt, a[u].y, o.y);
+          o.z = fmaf(wt, bb[u].x, o.z);
+          o.w = fmaf(wt, bb[u].y, o.w);
+        }
+        m_run = m_new;
+      }
+      if (dst) {
+        float* rec = dst + hh * C::REC;
+        store_dev2(rec + 4 + d4, o.x, o.y);
+        store_dev2(rec + 6 + d4, o.z, o.w);
+        if (d4 == 0) store_dev2(rec, m_run, L);
+      } else {
+        const float inv = 1.f / L;
+        *reinterpret_cast<float4*>(out + (static_cast<size_t>(b) * H + hh) * DH + d4) =
+            float4{o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+        if (lse && d4 == 0) lse[static_cast<size_t>(b) * H + hh] = kLn2 * (m_run + log2f(L));
+      }
+    }
+  };
   wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0)
-    last_s = __hip_atomic_fetch_add(tickets + static_cast<size_t>(b) * kTicketStride, 1u,
-                                    __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT) == static_cast<unsigned>(nc - 1);
-  __syncthreads();
-  if (!last_s) return;
-  // Each thread combines the chunk records of one head for 4 output dims,
-  // U chunks per round: the loads of a round are independent and overlap in
-  // flight, and rounds are combined online (log-sum-exp).
-  const float* sb = part + static_cast<size_t>(b) * num_chunks * H * C::REC;
-  const size_t cstride = static_cast<size_t>(H) * C::REC;
-  for (int i = threadIdx.x; i < H * (DH / 4); i += kThreads) {
-    const int hh = i / (DH / 4);
-    const int d4 = (i % (DH / 4)) * 4;
-    const float* r0 = sb + hh * C::REC;
-    float m_run = -INFINITY, L = 0.f;
-    float4 o = {0.f, 0.f, 0.f, 0.f};
-    constexpr int U = 8;
-    for (int c0 = 0; c0 < nc; c0 += U) {
-      float2 ml[U], a[U], bb[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {  // past the last chunk: reload it, weight 0
-        const float* r = r0 + min(c0 + u, nc - 1) * cstride;
-        ml[u] = load_dev2(r);
-        a[u] = load_dev2(r + 4 + d4);
-        bb[u] = load_dev2(r + 6 + d4);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (c0 + u >= nc) ml[u] = float2{-INFINITY, 0.f};
-      float m_new = m_run;
-#pragma unroll
-      for (int u = 0; u < U; ++u) m_new = fmaxf(m_new, ml[u].x);
-      const float sc = __builtin_amdgcn_exp2f(m_run - m_new);
-      L *= sc;
-      o.x *= sc;
-      o.y *= sc;
-      o.z *= sc;
-      o.w *= sc;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float wt = __builtin_amdgcn_exp2f(ml[u].x - m_new);
-        L = fmaf(wt, ml[u].y, L);
-        o.x = fmaf(wt, a[u].x, o.x);
-        o.y = fmaf(wt, a[u].y, o.y);
-        o.z = fmaf(wt, bb[u].x, o.z);
-        o.w = fmaf(wt, bb[u].y, o.w);
-      }
-      m_run = m_new;
-    }
-    const float inv = 1.f / L;
-    *reinterpret_cast<float4*>(out + (static_cast<size_t>(b) * H + hh) * DH + d4) =
-        float4{o.x * inv, o.y * inv, o.z * inv, o.w * inv};
-    if (lse && d4 == 0) lse[static_cast<size_t>(b) * H + hh] = kLn2 * (m_run + log2f(L));
+  const float* seq_records = part + static_cast<size_t>(b) * num_chunks * rset;
+  if (ng > 1) {
+    const int gi = c / kGroupChunks;
+    const int ncg = min(kGroupChunks, nc - gi * kGroupChunks);
+    unsigned* gt = seq_ticket + (1 + gi) * kTicketStride;
+    if (!last_of(gt, ncg)) return;
+    float* grec = groups + (static_cast<size_t>(b) * max_groups + gi) * rset;
+    merge(seq_records + static_cast<size_t>(gi) * kGroupChunks * rset, ncg, grec);
+    if (threadIdx.x == 0)  // ready for the next call
+      __hip_atomic_store(gt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_stores();
+    __syncthreads();
+    if (!last_of(seq_ticket, ng)) return;
+    merge(groups + static_cast<size_t>(b) * max_groups * rset, ng, nullptr);
+  } else {
+    if (!last_of(seq_ticket, nc)) return;
+    merge(seq_records, nc, nullptr);
   }
   if (threadIdx.x == 0)  // ready for the next call
-    __hip_atomic_store(tickets + static_cast<size_t>(b) * kTicketStride, 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(seq_ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int GT, int DH, int DR, bool GQA>
@@ -798,7 +837,8 @@ hipError_t launch_one(const gva_shape& s, const DecodePlan& plan, const DecodeAr
                      a.q, static_cast<const bf16_t*>(a.v_pool),
                      static_cast<const bf16_t*>(a.k_pool), a.block_table, a.seq_lens,
                      a.max_seq_len, s.H, s.G, s.max_blocks, s.num_blocks, plan.chunk_tokens,
-                     plan.num_chunks, a.q_len, a.q_scale, a.partials, a.tickets, a.out, a.lse);
+                     plan.num_chunks, plan.max_groups, a.q_len, a.q_scale, a.partials, a.tickets,
+                     a.out, a.lse);
   return hipGetLastError();
 }
 
@@ -867,8 +907,11 @@ DecodePlan plan_mfma_decode(const gva_shape& s, int max_seq_len, bool keys_separ
   if (chunk < kBlock) chunk = kBlock;
   p.chunk_tokens = static_cast<int>(chunk);
   p.num_chunks = max_seq_len > 0 ? static_cast<int>((max_seq_len + chunk - 1) / chunk) : 1;
-  p.partial_floats = static_cast<size_t>(s.B) * p.num_chunks * s.H * (s.d_h + 4);
-  p.ticket_bytes = ticket_bytes(s.B);
+  p.max_groups = p.num_chunks > 2 * kGroupChunks ? (p.num_chunks + kGroupChunks - 1) / kGroupChunks
+                                                 : 0;
+  p.partial_floats =
+      static_cast<size_t>(s.B) * (p.num_chunks + p.max_groups) * s.H * (s.d_h + 4);
+  p.ticket_bytes = ticket_bytes(s.B, p.max_groups);
   p.workspace_bytes = p.ticket_bytes + p.partial_floats * sizeof(float);
   return p;
 }

@@ -18,14 +18,21 @@ struct DecodePlan {
   size_t partial_floats;  // floats of split partial results
   size_t ticket_bytes;    // per-sequence completion counters at the workspace start
   size_t workspace_bytes;
+  int max_groups;         // chunk groups per sequence of a two-level merge (0: one level)
 };
 
-// Workspace = [B counters, one per 256 B][partial records].  A counter per
-// 256 B keeps the blocks of different sequences from contending for one
-// memory channel.  The counters must be zero before the first call; every
-// call leaves them zero.
+// Workspace = [B x (1 + max_groups) counters, one per 256 B][partial
+// records][group records].  A counter per 256 B keeps the blocks of
+// different sequences from contending for one memory channel.  The
+// counters must be zero before the first call; every call leaves them zero.
 constexpr int kTicketStride = 64;  // u32 elements between counters
-inline size_t ticket_bytes(int B) { return static_cast<size_t>(B) * kTicketStride * 4; }
+inline size_t ticket_bytes(int B, int max_groups = 0) {
+  return static_cast<size_t>(B) * (1 + max_groups) * kTicketStride * 4;
+}
+// A sequence split into more than 2 kGroupChunks chunks is merged in two
+// levels: the chunk records of each group of kGroupChunks by the group's
+// last block, then the group records by the last of those.
+constexpr int kGroupChunks = 16;
 
 enum { kKernelRef = 0, kKernelMfma = 1, kKernelPrefill = 2 };
 

@@ -146,7 +146,9 @@ gva_status gva_append_cache(const gva_shape* shape, const float* v_new,
  * upper bound on sequence length: per-sequence completion counters followed
  * by the split-context partial results.  A workspace must be zero-filled
  * once, when it is allocated; every call leaves its counters zero again, so
- * it can be reused (and captured in graphs) without clearing.  Calls that
+ * it can be reused (and captured in graphs) without clearing by calls with
+ * the same sizes and max_seq_len (the counters' place depends on them: a
+ * workspace that served other sizes must be zero-filled again).  Calls that
  * run concurrently need separate workspaces. */
 gva_status gva_decode_workspace_size(const gva_shape* shape,
                                      int32_t max_seq_len, size_t* bytes);

@@ -888,3 +888,36 @@ def test_gqa_many_query_tokens_one_token_is_the_single_query_call(g, gpu):
                                     x["block_table"], x["seq_lens"], x["max_seq_len"])
     torch.cuda.synchronize()
     assert torch.equal(o1[:, :, 0], o0) and torch.equal(l1[:, :, 0], l0)
+
+
+@pytest.mark.parametrize("L,lens", [
+    (4, [2050]),           # 33 chunks of 64: a third group holding only positions
+                           # past some queries' limits (records with max -inf)
+    (1, [32 * 64 + 1]),    # 33 chunks, one token in the third group
+    (2, [5000, 3000]),     # several groups per sequence, two sequences
+    (1, [2048, 700]),      # 32 chunks: one level
+])
+def test_two_level_merge(g, gpu, L, lens):
+    """More than 32 chunks per sequence: chunk records merge per group of 16,
+    then the group records; against the float64 oracle."""
+    cfg, x, h = _multi_case(gpu, 16, 4, 64, 48, 16, "bfloat16", L, lens=lens)
+    announce("two-level merge", L, lens)
+    qa = g.absorb_query_multi(x["q_nope"], x["q_rope"], x["M"], x["pos"],
+                              rope_base=cfg.rope_base)
+    ws = torch.zeros(max(16, g.decode_workspace_bytes_multi(
+        cfg.B, cfg.H, L, x["v_pool"], x["k_pool"], x["block_table"], x["max_seq_len"])),
+        dtype=torch.uint8, device=gpu)
+    out, lse = g.decode_attention_multi(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                        x["seq_lens"], x["max_seq_len"], workspace=ws)
+    torch.cuda.synchronize()
+    ref, ref_lse = o.gva_decode_materialized_queries(
+        h["q_nope"], h["q_rope"], h["M"], h["v_pool"], h["k_pool"], h["block_table"],
+        h["seq_lens"], base=cfg.rope_base)
+    assert_bf16_parity(cpu(out).double().numpy(), ref)
+    np.testing.assert_allclose(cpu(lse).double().numpy(), ref_lse, rtol=0, atol=1e-3)
+    # the call left every counter (sequence and group) at zero: a second call
+    # on the same workspace gives the same bits
+    out2, lse2 = g.decode_attention_multi(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                          x["seq_lens"], x["max_seq_len"], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out) and torch.equal(lse2, lse)
