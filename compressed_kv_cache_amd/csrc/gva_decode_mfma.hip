@@ -819,18 +819,10 @@ void decode_mfma_kernel(
     __hip_atomic_store(seq_ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int GT, int DH, int DR, bool GQA>
-hipError_t launch_one(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
-                      hipStream_t stream) {
+template <int GT, int DH, int DR, bool GQA, int NW, int WPE, int NSET>
+hipError_t launch_shape(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
+                        hipStream_t stream) {
   dim3 grid(plan.num_chunks, s.B);
-  // GVA at d_h = 64: 8 waves per block, 2 per SIMD.  d_h = 128 tiles (and
-  // the two streams of GQA) need the whole register file, 1 wave per SIMD:
-  // 4 waves per block.
-  constexpr int NW = (DH == 64 && !GQA) ? 8 : 4;
-  constexpr int WPE = (DH == 64 && !GQA) ? 2 : 1;
-  // three register sets where tiles are narrow (GQA d_h = 64, and one or
-  // two value groups per head tile, where each tile is only 2-4 KB)
-  constexpr int NSET = (GQA && DH == 64) || GT < 4 ? 3 : 2;
   if ((s.H / 16) > NW || NW % (s.H / 16) != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL((decode_mfma_kernel<GT, DH, DR, GQA, NW, WPE, NSET>), grid, dim3(64 * NW),
                      0, stream,
@@ -840,6 +832,23 @@ hipError_t launch_one(const gva_shape& s, const DecodePlan& plan, const DecodeAr
                      plan.num_chunks, plan.max_groups, a.q_len, a.q_scale, a.partials, a.tickets,
                      a.out, a.lse);
   return hipGetLastError();
+}
+
+template <int GT, int DH, int DR, bool GQA>
+hipError_t launch_one(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
+                      hipStream_t stream) {
+  // 4 waves per block, 1 per SIMD, each with the whole register file.  At
+  // d_h = 64 this beat 8 waves at 2 per SIMD by about 5 % on the three
+  // d_h = 64 workloads (fewer wave records to merge, each wave streaming
+  // twice the tiles); 8 waves remain for GVA d_h = 64 with more than 4
+  // head tiles (a block holds one wave per head tile at least).
+  // Three register sets where tiles are narrow (GQA d_h = 64, and one or
+  // two value groups per head tile, where each tile is only 2-4 KB).
+  constexpr int NSET = (GQA && DH == 64) || GT < 4 ? 3 : 2;
+  if constexpr (DH == 64 && !GQA) {
+    if (s.H / 16 > 4) return launch_shape<GT, DH, DR, GQA, 8, 2, NSET>(s, plan, a, stream);
+  }
+  return launch_shape<GT, DH, DR, GQA, 4, 1, NSET>(s, plan, a, stream);
 }
 
 typedef hipError_t (*launch_fn)(const gva_shape&, const DecodePlan&, const DecodeArgs&,
