@@ -837,16 +837,17 @@ hipError_t launch_shape(const gva_shape& s, const DecodePlan& plan, const Decode
 template <int GT, int DH, int DR, bool GQA>
 hipError_t launch_one(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
                       hipStream_t stream) {
-  // 4 waves per block, 1 per SIMD, each with the whole register file.  At
-  // d_h = 64 this beat 8 waves at 2 per SIMD by about 5 % on the three
-  // d_h = 64 workloads (fewer wave records to merge, each wave streaming
-  // twice the tiles); 8 waves remain for GVA d_h = 64 with more than 4
-  // head tiles (a block holds one wave per head tile at least).
-  // Three register sets where tiles are narrow (GQA d_h = 64, and one or
-  // two value groups per head tile, where each tile is only 2-4 KB).
+  // Single query token (four value groups per head tile): 4 waves per
+  // block, 1 per SIMD, each with the whole register file.  At d_h = 64 this
+  // beat 8 waves at 2 per SIMD by 3-5 % on the three d_h = 64 workloads
+  // (fewer wave records to merge, each wave streaming twice the tiles).
+  // With several query tokens (one or two groups per head tile, tiles of
+  // 2-4 KB) and with more than 4 head tiles, GVA at d_h = 64 keeps 8 waves
+  // at 2 per SIMD (4 were up to 40 % slower there).  Three register sets
+  // where tiles are narrow (GQA d_h = 64, and one or two groups per tile).
   constexpr int NSET = (GQA && DH == 64) || GT < 4 ? 3 : 2;
   if constexpr (DH == 64 && !GQA) {
-    if (s.H / 16 > 4) return launch_shape<GT, DH, DR, GQA, 8, 2, NSET>(s, plan, a, stream);
+    if (GT < 4 || s.H / 16 > 4) return launch_shape<GT, DH, DR, GQA, 8, 2, NSET>(s, plan, a, stream);
   }
   return launch_shape<GT, DH, DR, GQA, 4, 1, NSET>(s, plan, a, stream);
 }
