@@ -7,8 +7,9 @@
 // parts so the products carry ~16 mantissa bits; the cache values themselves
 // are exact bf16.
 //
-// Work split: block (c, b) owns chunk c of sequence b and runs 8 waves
-// (d_h = 64) or 4 (d_h = 128, GQA).  Query heads come in tiles of 16 (one
+// Work split: block (c, b) owns chunk c of sequence b and runs 4 waves (8
+// for d_h = 64 with several query tokens or more than 4 head tiles; the
+// launcher's comment gives the measurements).  Query heads come in tiles of 16 (one
 // MFMA column each); a head tile covers GT = 16/(H/G) whole value groups.
 // With H/16 head tiles the waves are divided between head tiles, and the
 // waves of a head tile take the chunk's 16-token tiles in turn, two per step:
@@ -19,8 +20,9 @@
 //   2. the value rows go to a wave-private LDS tile (XOR-swizzled rows,
 //      conflict-free for the row writes and the transpose reads);
 //   3. scores S^T[token][head] = V_g . qa^T per group (16x16x32 MFMAs, V read
-//      back from LDS) plus k_rope . qr^T (16x16x16), keeping for each head
-//      its own group's sum;
+//      back from LDS) plus k_rope . qr^T (16x16x16, in an accumulator of
+//      its own: no accumulator chain switches MFMA shapes), keeping for
+//      each head its own group's sum;
 //   4. the running max/sum of each head absorb the pair's 32 scores (log2
 //      units); the max is raised only when a score exceeds it by 2^8, so the
 //      accumulator is rarely rescaled;
@@ -31,7 +33,8 @@
 // chunk, head).  Each block then takes a ticket from its sequence's counter;
 // the block that finishes last merges the chunk records of that sequence
 // into the output (log-sum-exp) and resets the counter, so the whole decode
-// is one launch.
+// is one launch (a sequence of more than 32 chunks merges in two levels,
+// per group of 16 chunks first).
 #include "gva_device.h"
 #include "gva_internal.h"
 
@@ -665,7 +668,8 @@ void decode_mfma_kernel(
   float* pb = part + (static_cast<size_t>(b) * num_chunks + c) * H * C::REC;
   const float nan = __builtin_nanf("");
   // VW output dims per thread: 2 where that gives every thread of the block
-  // one item (d_h = 64 with 8 waves), else 4
+  // one item (d_h = 64 with 8 waves), else 4 (d_h = 64 with 4 waves: again
+  // one item per thread)
   constexpr int VW = (16 * DH <= 2 * kThreads) ? 2 : 4;
   for (int i = threadIdx.x; i < nht * 16 * (DH / VW); i += kThreads) {
     const int hh = i / (DH / VW);          // head within the block's H
