@@ -72,6 +72,8 @@ def parse():
                     help="skip the rotated-reconstructed-key decode measurement")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill leg (every query token of the context at once)")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the plain-read rate of the same cache buffers")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--ingest-counters", nargs=4, metavar="DIR")
@@ -318,6 +320,12 @@ def main():
         "gqa_cache_bytes_same_shape": tokens * 2 * cfg.G * cfg.d_h * esize,
     }
 
+    if not args.no_read_probe:
+        extra["read_probe"] = bench_read_probe(torch, gva, [vp for vp, _ in pools], dev,
+                                               args.steps)
+        extra["read_probe"]["decode_over_probe_rate"] = (
+            achieved / extra["read_probe"]["cache_v_pool"]["GBps"])
+
     if not args.no_gqa and cfg.cache_dtype == "bfloat16":
         extra["gqa"] = bench_gqa(torch, gva, syn, cfg0, dev, args.steps, args.warmup)
         extra["gqa"]["time_ratio_gva_over_gqa"] = dec_avg_ms * 1e3 / extra["gqa"]["us_avg"]
@@ -382,6 +390,47 @@ def main():
         "extra": extra,
     }
     print(json.dumps(line))
+
+
+def bench_read_probe(torch, gva, v_pools, dev, steps):
+    """Achievable read rate beside the 8 TB/s peak: the plain streaming read
+    (gva_stream_read_probe: the decode's 16-byte non-temporal loads, no
+    arithmetic) of (a) each rotating copy's value pool, the bulk of the
+    cache bytes, one launch per copy like one decode launch, and (b) one
+    1 GiB buffer in one launch, where the launch's fixed costs vanish.
+    HIP events on the launch stream around graph replays."""
+    out = torch.empty(gva.PROBE_BLOCKS, dtype=torch.int32, device=dev)
+
+    def rate(bufs, launches):
+        g = torch.cuda.CUDAGraph()
+        for b in bufs:
+            gva.stream_read_probe(b, out=out)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(launches):
+                gva.stream_read_probe(bufs[i % len(bufs)], out=out)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, -(-steps // launches))
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) / (reps * launches) * 1e3
+        nbytes = bufs[0].numel() * bufs[0].element_size()
+        return {"bytes": nbytes, "us_avg": us, "GBps": nbytes / (us * 1e-6) / 1e9,
+                "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+
+    res = {"kernel": "gva_stream_read_probe",
+           "cache_v_pool": rate(v_pools, max(len(v_pools), 8))}
+    big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    res["one_gib"] = rate([big], 4)
+    del big
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_multi(torch, gva, syn, cfg, dev, steps, warmup, L):

@@ -28,10 +28,13 @@ _I32 = ctypes.c_int32
 _F32 = ctypes.c_float
 _SIZE = ctypes.c_size_t
 
+PROBE_BLOCKS = 1024  # GVA_PROBE_BLOCKS: words written by gva_stream_read_probe
+
 SIGNATURES = {
     "gva_abi_version": (_I32, []),
     "gva_status_string": (ctypes.c_char_p, [_I32]),
     "gva_cache_scalars_per_token": (ctypes.c_uint64, [_SHAPE]),
+    "gva_stream_read_probe": (_I32, [_P, ctypes.c_uint64, _P, _P]),
     "gva_absorb_query": (_I32, [_SHAPE, _P, _P, _P, _P, _F32, _F32, _P, _P]),
     "gva_append_cache": (_I32, [_SHAPE, _P, _P, _P, _P, _F32, _P, _P, _P]),
     "gva_decode_workspace_size": (_I32, [_SHAPE, _I32, ctypes.POINTER(_SIZE)]),

@@ -16,7 +16,8 @@ LIB = os.path.join(PKG, "libgva.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["gva_api.cpp", "gva_prologue.hip", "gva_decode_ref.hip",
-           "gva_decode_mfma.hip", "gva_decode_rope.hip", "gva_prefill.hip"]
+           "gva_decode_mfma.hip", "gva_decode_rope.hip", "gva_prefill.hip",
+           "gva_probe.hip"]
 
 # Packed fp32 instructions are switched off for all device code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -20,6 +20,8 @@ hipError_t launch_prefill(const gva_shape& s, int q_len, const float* qa, const 
                           const void* k_pool, const int32_t* block_table,
                           const int32_t* seq_lens, int max_seq_len, bool keys_separate,
                           float q_scale, float* out, float* lse, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* xor_out, int blocks,
+                              hipStream_t stream);
 bool rope_keys_supported(const gva_shape& s);
 DecodePlan plan_rope_keys(const gva_shape& s, int max_seq_len);
 hipError_t launch_rope_keys(const gva_shape& s, const DecodePlan& plan, const float* q,
@@ -253,6 +255,17 @@ const char* gva_status_string(int32_t status) {
     case GVA_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
   }
+}
+
+gva_status gva_stream_read_probe(const void* buf, uint64_t bytes, uint32_t* xor_out,
+                                 void* stream) {
+  if (!xor_out || (!buf && bytes > 0)) return GVA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(buf) % 16 || bytes % 16 ||
+      reinterpret_cast<uintptr_t>(xor_out) % 4)
+    return GVA_ERR_ALIGN;
+  return to_status(gva::launch_stream_read(buf, static_cast<size_t>(bytes), xor_out,
+                                           GVA_PROBE_BLOCKS,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 uint64_t gva_cache_scalars_per_token(const gva_shape* shape) {

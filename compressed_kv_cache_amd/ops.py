@@ -56,6 +56,25 @@ def cache_scalars_per_token(G, d_h, d_r):
     return int(_lib.load().gva_cache_scalars_per_token(ctypes.byref(s)))
 
 
+def stream_read_probe(buf, out=None):
+    """Plain streaming read of a contiguous device tensor's bytes (a
+    calibration of the achievable read rate; gva_stream_read_probe).
+    Returns an int32 tensor of PROBE_BLOCKS words on buf's device whose XOR
+    is the XOR of every 32-bit word of buf."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous torch.Tensor")
+    dev = buf.device
+    if out is None:
+        out = torch.empty(_lib.PROBE_BLOCKS, dtype=torch.int32, device=dev)
+    _need(out, "out", torch.int32, dev, 1)
+    if out.numel() != _lib.PROBE_BLOCKS:
+        raise ValueError(f"out must hold {_lib.PROBE_BLOCKS} words")
+    nbytes = buf.numel() * buf.element_size()
+    check("gva_stream_read_probe",
+          _lib.load().gva_stream_read_probe(_ptr(buf), nbytes, _ptr(out), _stream(dev)))
+    return out
+
+
 def absorb_query(q_nope, q_rope, M, pos, softmax_scale=None, rope_base=10000.0,
                  out=None):
     """qa[B,H,d_h+d_r] = s * [q_nope M_h^T | R(pos) q_rope] (gva_absorb_query)."""

@@ -106,6 +106,24 @@ const char* gva_status_string(int32_t status);
  * it differs": N_GVA = T*G*d_h + T*d_r).  Returns 0 for a NULL shape. */
 uint64_t gva_cache_scalars_per_token(const gva_shape* shape);
 
+/* Calibration helper, not a step of the method: the decode is bound by the
+ * rate of its cache read (onedev.kr review, "Premises and limits"), and
+ * this call states the achievable read rate of the same bytes with the
+ * decode's load form.  It reads `bytes` bytes at `buf` with 16-byte
+ * non-temporal loads, GVA_PROBE_BLOCKS blocks each over one contiguous
+ * range, and block i writes the XOR of the 32-bit words of its range to
+ * xor_out[i] (0 for an empty range); the XOR of all GVA_PROBE_BLOCKS words
+ * is the XOR of every 32-bit word of the buffer.
+ *   buf: device, 16B (may be NULL when bytes == 0); bytes: a multiple of 16;
+ *   xor_out: device, GVA_PROBE_BLOCKS uint32, 4-byte aligned, all written;
+ *   stream: hipStream_t or NULL.
+ * Errors (before any HIP call): GVA_ERR_NULL (xor_out NULL, or buf NULL with
+ * bytes > 0), GVA_ERR_ALIGN (buf not 16-byte aligned, bytes not a multiple
+ * of 16, or xor_out not 4-byte aligned); a failed launch, GVA_ERR_HIP. */
+#define GVA_PROBE_BLOCKS 1024
+gva_status gva_stream_read_probe(const void* buf, uint64_t bytes, uint32_t* xor_out,
+                                 void* stream);
+
 /* Absorb each head's fixed key map into its query, once per query token
  * (onedev.kr review, "How it works"; bisque.today explainer, Equation 7):
  *

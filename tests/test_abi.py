@@ -312,3 +312,18 @@ def test_batch_past_grid_bound_is_unsupported(g):
     assert _ws(g, _shape(g, B=16383, G=4))[0] == 0
     assert _ws(g, _shape(g, B=16384, G=4))[0] == 3
     assert _ws(g, _shape(g, B=70000, G=1, H=4))[0] == 3
+
+
+def test_stream_read_probe_validation(g):
+    """The read-rate probe rejects missing and misaligned buffers before any
+    HIP call."""
+    P = ctypes.c_void_p
+    f = g.lib.gva_stream_read_probe
+    assert f(P(0x10000), 16, None, None) == 1           # no output
+    assert f(None, 16, P(0x10000), None) == 1           # no buffer for 16 bytes
+    assert f(P(0x10008), 16, P(0x10000), None) == 4     # buffer not 16B aligned
+    assert f(P(0x10000), 24, P(0x10000), None) == 4     # bytes not a multiple of 16
+    assert f(P(0x10000), 16, P(0x10002), None) == 4     # output not 4B aligned
+    from compressed_kv_cache_amd._lib import PROBE_BLOCKS
+    assert PROBE_BLOCKS == int(re.search(r"#define GVA_PROBE_BLOCKS (\d+)",
+                                         open(HEADER).read()).group(1))

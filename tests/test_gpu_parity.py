@@ -921,3 +921,27 @@ def test_two_level_merge(g, gpu, L, lens):
                                           x["seq_lens"], x["max_seq_len"], workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(out2, out) and torch.equal(lse2, lse)
+
+
+# ---- read-rate probe (measurement helper) ----
+
+@pytest.mark.parametrize("nbytes", [0, 16, 16 * 1023, 16 * 1025 + 16 * 7, (1 << 20) + 48,
+                                    71303168])
+def test_stream_read_probe_checksum(g, gpu, nbytes):
+    """Every byte is read: the XOR of the probe's per-block words equals the
+    XOR of all 32-bit words of the buffer (computed on the host), for sizes
+    below, at and above one 16-byte unit per block, ragged per-block ranges
+    and the 350M-shaped cache size; the output is fully overwritten."""
+    announce(f"stream_read_probe bytes={nbytes}")
+    gen = torch.Generator(device="cpu").manual_seed(nbytes % 9973)
+    host = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, generator=gen)
+    buf = host.to(gpu)
+    from compressed_kv_cache_amd._lib import PROBE_BLOCKS
+    out = torch.full((PROBE_BLOCKS,), -1, dtype=torch.int32, device=gpu)
+    g.stream_read_probe(buf, out=out)
+    torch.cuda.synchronize()
+    words = out.cpu().numpy().view(np.uint32)
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32)) if nbytes else np.uint32(0)
+    assert np.bitwise_xor.reduce(words) == want
+    if nbytes == 0:
+        assert not words.any()
