@@ -329,6 +329,8 @@ def main():
     if not args.no_gqa and cfg.cache_dtype == "bfloat16":
         extra["gqa"] = bench_gqa(torch, gva, syn, cfg0, dev, args.steps, args.warmup)
         extra["gqa"]["time_ratio_gva_over_gqa"] = dec_avg_ms * 1e3 / extra["gqa"]["us_avg"]
+        extra["gqa"]["byte_ratio_gva_over_gqa"] = (
+            cache_bytes / extra["gqa_cache_bytes_same_shape"])
     if not args.no_multi:
         del pools
         torch.cuda.empty_cache()
