@@ -41,7 +41,8 @@ struct PrologueArgs {
   int pos_offset;
   int q_len;           // tokens per sequence (L): token i sits at that position - (L-1) + i
   int B, H, G, d_h, d_n, d_r, bs, max_blocks, num_blocks;
-  int absorb_blocks;   // blocks [0, absorb_blocks) absorb, the rest append
+  int absorb_blocks;   // blocks [0, absorb_blocks) absorb the content slice,
+  int rope_blocks;     // the next rope_blocks rotate the position slice, the rest append
   int vec4;            // q_nope and M rows 16-byte aligned (d_n % 4 == 0)
 };
 
@@ -73,36 +74,16 @@ __device__ __forceinline__ void rotate_f64(double x0, double x1, int pos, double
 // (v_mfma_f32_16x16x4_f32: lane l feeds A[l%16][l/16] and B[l/16][l%16] and
 // holds D[4(l/16)+r][l%16]).  Lane group l/16 sums the contiguous n range
 // [kg*K4, kg*K4 + K4), K4 = ceil(d_n/4), so each lane's loads are
-// contiguous.  The waves of (h, b0) also write the rotated position slice
-// qa[b][h][d_h + 2i, 2i+1] = s * R(pos_b) q_rope[b][h] (float64 rotation).
-// The fixed map M_h folds into the query once per token (onedev.kr review,
+// contiguous.  The fixed map M_h folds into the query once per token (onedev.kr review,
 // "How it works"; bisque.today, Equation 7).
-__device__ __forceinline__ void absorb_block(const PrologueArgs& a, const RopeTable& rt,
-                                             int id) {
+__device__ __forceinline__ void absorb_block(const PrologueArgs& a, int id) {
   const int lane = threadIdx.x;
   const int DT = a.d_h / 16;
   const int et = id % DT, rest = id / DT;
   const int h = rest % a.H, b0 = (rest / a.H) * 16;
   const int R = a.B * a.q_len;  // rows
   const int li = lane & 15, kg = lane >> 4;
-  const int half = a.d_r / 2;
   const int dq = a.d_h + a.d_r;
-
-  // position-slice inputs of this lane's first pair, loaded with the rest
-  // (no positional slice when d_r = 0)
-  const int npairs = 16 * half;
-  const int hd = max(half, 1);
-  int pi = et * 64 + lane;
-  int p_seq = min(pi / hd, 15), p_i = pi % hd;
-  int p_b = min(b0 + p_seq, R - 1);
-  float x0 = 0.f, x1 = 0.f;
-  int p_pos = 0;
-  if (half > 0) {  // uniform
-    const float* xr = a.q_rope + head_row(a, p_b, h) * a.d_r + 2 * p_i;
-    x0 = xr[0];
-    x1 = xr[1];
-    p_pos = row_pos(a, p_b);
-  }
 
   const int bq = min(b0 + li, R - 1);
   const float* qrow = a.q_nope + head_row(a, bq, h) * a.d_n;
@@ -156,26 +137,28 @@ __device__ __forceinline__ void absorb_block(const PrologueArgs& a, const RopeTa
     const int b = b0 + 4 * kg + r;
     if (b < R) a.qa[head_row(a, b, h) * dq + et * 16 + li] = a.scale * acc[r];
   }
+}
 
+// Position slice of the absorbed query, one lane per rotary pair (row r,
+// head h, pair i), in blocks of its own so that its float64 rotation runs
+// beside the content products rather than after them:
+//   qa[r][h][d_h + 2i, 2i+1] = s * R(pos_r) q_rope[r][h][2i, 2i+1]
+// (onedev.kr review, "How it differs": the query's position slice is
+// rotated to the query's own position).
+__device__ __forceinline__ void rope_block(const PrologueArgs& a, const RopeTable& rt, int id) {
+  const int half = a.d_r / 2;
+  const int per_row = a.H * half;
+  const int idx = id * kThreads + static_cast<int>(threadIdx.x);
+  if (idx >= a.B * a.q_len * per_row) return;
+  const int r = idx / per_row, rem = idx - r * per_row;
+  const int h = rem / half, i = rem - h * half;
+  const float* xr = a.q_rope + head_row(a, r, h) * a.d_r + 2 * i;
+  double y0, y1;
+  rotate_f64(xr[0], xr[1], row_pos(a, r), rt.theta[i], &y0, &y1);
   const double sc = static_cast<double>(a.scale);
-  while (half > 0) {
-    if (pi < npairs && b0 + p_seq < R) {
-      double y0, y1;
-      rotate_f64(x0, x1, p_pos, rt.theta[p_i], &y0, &y1);
-      float* dst = a.qa + head_row(a, p_b, h) * dq + a.d_h + 2 * p_i;
-      dst[0] = static_cast<float>(sc * y0);
-      dst[1] = static_cast<float>(sc * y1);
-    }
-    pi += DT * 64;
-    if (pi >= npairs) break;
-    p_seq = pi / half;
-    p_i = pi % half;
-    p_b = min(b0 + p_seq, R - 1);
-    const float* xr = a.q_rope + head_row(a, p_b, h) * a.d_r + 2 * p_i;
-    x0 = xr[0];
-    x1 = xr[1];
-    p_pos = row_pos(a, p_b);
-  }
+  float* dst = a.qa + head_row(a, r, h) * (a.d_h + a.d_r) + a.d_h + 2 * i;
+  dst[0] = static_cast<float>(sc * y0);
+  dst[1] = static_cast<float>(sc * y1);
 }
 
 __device__ __forceinline__ void store4(float* p, float x0, float x1, float x2, float x3) {
@@ -230,9 +213,11 @@ template <typename CT>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a, RopeTable rt) {
   const int id = blockIdx.x;
   if (id < a.absorb_blocks)
-    absorb_block(a, rt, id);
+    absorb_block(a, id);
+  else if (id < a.absorb_blocks + a.rope_blocks)
+    rope_block(a, rt, id - a.absorb_blocks);
   else
-    append_block<CT>(a, rt, id - a.absorb_blocks);
+    append_block<CT>(a, rt, id - a.absorb_blocks - a.rope_blocks);
 }
 
 RopeTable rope_table(int d_r, double base) {
@@ -278,8 +263,11 @@ hipError_t launch_prologue(const gva_shape& s, const float* q_nope, const float*
   a.absorb_blocks = q_nope ? static_cast<int>(s.H * ((rows + 15) / 16) * (s.d_h / 16)) : 0;
   a.vec4 = q_nope && s.d_n % 4 == 0 && reinterpret_cast<uintptr_t>(q_nope) % 16 == 0 &&
            reinterpret_cast<uintptr_t>(M) % 16 == 0;
+  const long long rope_items = q_nope ? rows * s.H * (s.d_r / 2) : 0;
+  a.rope_blocks = static_cast<int>((rope_items + kThreads - 1) / kThreads);
   const long long append_items = v_new ? rows * (s.G * s.d_h / 4 + s.d_r / 2) : 0;
-  const int blocks = a.absorb_blocks + static_cast<int>((append_items + kThreads - 1) / kThreads);
+  const int blocks = a.absorb_blocks + a.rope_blocks +
+                     static_cast<int>((append_items + kThreads - 1) / kThreads);
   if (blocks == 0) return hipSuccess;
   const RopeTable rt = rope_table(s.d_r, base);
   if (s.cache_dtype == GVA_BF16)
