@@ -172,6 +172,9 @@ def main():
         print(json.dumps({"error": "this benchmark measures one GPU: --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print(json.dumps({"error": "--steps must be >= 1 and --warmup >= 0"}))
+        sys.exit(2)
     import torch
     if args.copy_calibration:
         copy_calibration(torch, max(1, args.steps))
@@ -258,6 +261,15 @@ def main():
     with torch.cuda.graph(g_step):
         for i in range(S):
             step(i)
+    # the timed region holds exactly `steps` steps: steps // S replays of the
+    # S-step graph and one replay of a graph of the remaining steps
+    full, rem = divmod(args.steps, S)
+    g_rem = None
+    if rem:
+        g_rem = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_rem):
+            for i in range(rem):
+                step(i)
     with torch.cuda.graph(g_dec):
         for i in range(S):
             decode_only(i)
@@ -268,14 +280,18 @@ def main():
     reps = max(1, -(-args.steps // S))
     for _ in range(2):
         g_step.replay()
+    if g_rem is not None:
+        g_rem.replay()
     torch.cuda.synchronize()
     t0.record()
-    for _ in range(reps):
+    for _ in range(full):
         g_step.replay()
+    if g_rem is not None:
+        g_rem.replay()
     t1.record()
     torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / (reps * S)
-    steps_timed = reps * S
+    steps_timed = full * S + rem
+    ms_per_step = t0.elapsed_time(t1) / steps_timed
 
     # decode launches alone: one event pair per graph of R launches
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
