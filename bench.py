@@ -394,7 +394,8 @@ def main():
             "accumulate": "f32",
             "step": "gva_decode_step: append+absorb (1 launch) + decode with in-kernel merge "
                     "(1 launch)",
-            "timing": "HIP graphs of max(R, 8) steps replayed back to back",
+            "timing": "HIP graphs of max(R, 8) steps replayed back to back, plus one graph "
+                      "of the remaining steps: exactly --steps steps timed",
             "rotating_cache_copies": R,
         },
         "roofline": {
