@@ -853,6 +853,12 @@ hipError_t launch_one(const gva_shape& s, const DecodePlan& plan, const DecodeAr
   if constexpr (DH == 64 && !GQA) {
     if (GT < 4 || s.H / 16 > 4) return launch_shape<GT, DH, DR, GQA, 8, 2, NSET>(s, plan, a, stream);
   }
+  // d_h = 128 with one group per head tile (several query tokens) and more
+  // than 4 head tiles: 8 waves, one per head tile (4 KB tiles, so eight
+  // waves' tiles fit in LDS; with two groups per tile the registers spill)
+  if constexpr (DH == 128 && !GQA && GT == 1) {
+    if (s.H / 16 > 4) return launch_shape<GT, DH, DR, GQA, 8, 2, NSET>(s, plan, a, stream);
+  }
   return launch_shape<GT, DH, DR, GQA, 4, 1, NSET>(s, plan, a, stream);
 }
 
@@ -880,8 +886,11 @@ launch_fn pick(const gva_shape& s, bool gqa, int q_len) {
   if (s.cache_dtype != GVA_BF16 || s.H % 16 != 0) return nullptr;
   const int nht = s.H / 16;
   if (nht & (nht - 1)) return nullptr;
-  if (nht > (s.d_h == 64 && !gqa ? 8 : 4)) return nullptr;
   const int hpg = s.H / s.G;  // columns per group
+  // 8 head tiles need 8 waves: at d_h = 64, or at d_h = 128 with one group
+  // per head tile (H/G = 16 columns per group)
+  const bool eight = !gqa && (s.d_h == 64 || (s.d_h == 128 && hpg == 16));
+  if (nht > (eight ? 8 : 4)) return nullptr;
   if (gqa) {
     if (hpg != 4 || q_len != 1) return nullptr;
     if (s.d_h == 64) return launch_one<4, 64, 0, true>;

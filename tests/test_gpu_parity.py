@@ -530,6 +530,8 @@ def _multi_case(gpu, H, G, d_h, d_n, d_r, dtype, L, lens=MULTI_LENS, append=Fals
     (16, 4, 64, 48, 16, "bfloat16", 2),     # matrix cores, two groups per head tile
     (16, 4, 64, 40, 24, "bfloat16", 4),
     (32, 8, 128, 96, 32, "bfloat16", 2),    # matrix cores, d_h 128
+    (32, 8, 128, 96, 32, "bfloat16", 4),    # d_h 128, 8 head tiles of one group: 8 waves
+    (32, 8, 128, 128, 0, "bfloat16", 4),
     (16, 4, 64, 64, 0, "bfloat16", 4),      # no positional slice
     (8, 8, 32, 24, 8, "float32", 3),        # vector path
     (16, 4, 64, 48, 16, "float32", 4),      # vector path, fp32 cache
