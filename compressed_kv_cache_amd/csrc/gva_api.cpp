@@ -238,6 +238,24 @@ gva_status decode(const gva_shape* shape, int32_t q_len, const float* q, float q
   return to_status(gva::launch_decode_ref(s, plan, a, strm));
 }
 
+// Ordinary RoPE on the reconstructed key: d_n is the key width d_k, no
+// separate positional slice (d_r = 0).
+gva_status check_rope_keys(const gva_shape* shape, int32_t max_seq_len, float softmax_scale,
+                           float rope_base) {
+  if (!shape) return GVA_ERR_NULL;
+  gva_status st = check_cache_shape(*shape);
+  if (st != GVA_OK) return st;
+  if (shape->d_n < 2 || shape->d_n % 2 || shape->d_r != 0) return GVA_ERR_SHAPE;
+  if (!(rope_base > 0.f) || !isfinite(rope_base) || !isfinite(softmax_scale))
+    return GVA_ERR_SHAPE;
+  if (max_seq_len < 0 ||
+      static_cast<long long>(max_seq_len) >
+          static_cast<long long>(shape->max_blocks) * shape->block_size)
+    return GVA_ERR_SHAPE;
+  if (!gva::rope_keys_supported(*shape)) return GVA_ERR_UNSUPPORTED;
+  return GVA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -434,24 +452,6 @@ gva_status gva_decode_step(const gva_shape* shape, const float* q_nope, const fl
   return gva_decode_step_multi(shape, 1, q_nope, q_rope, M, softmax_scale, rope_base, v_new,
                                k_new, v_pool, k_pool, block_table, seq_lens, max_seq_len,
                                workspace, workspace_bytes, out, lse, stream);
-}
-
-// Ordinary RoPE on the reconstructed key: d_n is the key width d_k, no
-// separate positional slice (d_r = 0).
-gva_status check_rope_keys(const gva_shape* shape, int32_t max_seq_len, float softmax_scale,
-                           float rope_base) {
-  if (!shape) return GVA_ERR_NULL;
-  gva_status st = check_cache_shape(*shape);
-  if (st != GVA_OK) return st;
-  if (shape->d_n < 2 || shape->d_n % 2 || shape->d_r != 0) return GVA_ERR_SHAPE;
-  if (!(rope_base > 0.f) || !isfinite(rope_base) || !isfinite(softmax_scale))
-    return GVA_ERR_SHAPE;
-  if (max_seq_len < 0 ||
-      static_cast<long long>(max_seq_len) >
-          static_cast<long long>(shape->max_blocks) * shape->block_size)
-    return GVA_ERR_SHAPE;
-  if (!gva::rope_keys_supported(*shape)) return GVA_ERR_UNSUPPORTED;
-  return GVA_OK;
 }
 
 gva_status gva_decode_rope_keys_workspace_size(const gva_shape* shape, int32_t max_seq_len,
