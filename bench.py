@@ -74,6 +74,8 @@ def parse():
                     help="skip the prefill leg (every query token of the context at once)")
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip the plain-read rate of the same cache buffers")
+    ap.add_argument("--no-dr-sweep", action="store_true",
+                    help="skip the decode timed over positional widths d_r = 0, 16, 24, 32")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--ingest-counters", nargs=4, metavar="DIR")
@@ -347,6 +349,12 @@ def main():
         extra["gqa"]["time_ratio_gva_over_gqa"] = dec_avg_ms * 1e3 / extra["gqa"]["us_avg"]
         extra["gqa"]["byte_ratio_gva_over_gqa"] = (
             cache_bytes / extra["gqa_cache_bytes_same_shape"])
+    if not args.no_dr_sweep and cfg.cache_dtype == "bfloat16" and cfg.name == "decode_350m":
+        del pools
+        torch.cuda.empty_cache()
+        pools = None
+        extra["dr_sweep"] = bench_dr_sweep(torch, gva, syn, cfg0, dev, args.steps,
+                                           extra.get("gqa", {}).get("us_avg"))
     if not args.no_multi:
         del pools
         torch.cuda.empty_cache()
@@ -450,6 +458,68 @@ def bench_read_probe(torch, gva, v_pools, dev, steps):
     del big
     torch.cuda.empty_cache()
     return res
+
+
+def bench_dr_sweep(torch, gva, syn, cfg, dev, steps, gqa_us):
+    """The decode at one shape over positional widths d_r (d_n = d_h - d_r),
+    same protocol as the headline decode (graphs over rotating cache copies,
+    HIP events on the launch stream).  Beside each: the cache bytes, the
+    fraction of the 8 TB/s peak, the closed-form GVA/GQA byte ratio
+    1/2 + d_r/(2 G d_h) and the time ratio against the same-shape GQA decode
+    (which does not depend on d_r)."""
+    rows = []
+    for d_r in (0, 16, 24, 32):
+        c = syn.with_overrides(cfg, d_r=d_r, d_n=cfg.d_h - d_r)
+        y = syn.make_gva_inputs(c, device=dev)
+        tokens = int(y["seq_lens_host"].sum())
+        byts = tokens * (c.G * c.d_h + c.d_r) * 2
+        pool_bytes = (y["v_pool"].numel() + y["k_pool"].numel()) * 2
+        R = max(1, math.ceil(ROTATE_BYTES / pool_bytes))
+        pools = [(y["v_pool"], y["k_pool"])] + [
+            (y["v_pool"].clone(), y["k_pool"].clone()) for _ in range(R - 1)]
+        qa = gva.absorb_query(y["q_nope"], y["q_rope"], y["M"], y["pos"],
+                              rope_base=c.rope_base)
+        ws = torch.zeros(max(16, gva.decode_workspace_bytes(
+            c.B, c.H, y["v_pool"], y["k_pool"], y["block_table"], y["max_seq_len"])),
+            dtype=torch.uint8, device=dev)
+        out = torch.empty((c.B, c.H, c.d_h), dtype=torch.float32, device=dev)
+        lse = torch.empty((c.B, c.H), dtype=torch.float32, device=dev)
+
+        def launch(i):
+            vp, kp = pools[i % R]
+            gva.decode_attention(qa, vp, kp, y["block_table"], y["seq_lens"],
+                                 y["max_seq_len"], workspace=ws, out=out, lse=lse)
+
+        S = max(R, 8)
+        for i in range(S):
+            launch(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(S):
+                launch(i)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(2, -(-steps // S))
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) / (reps * S) * 1e3
+        row = {"d_r": d_r, "d_n": c.d_n, "us_avg": us, "cache_bytes": byts,
+               "GBps": byts / (us * 1e-6) / 1e9,
+               "frac_of_peak": byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+               "byte_ratio_gva_over_gqa": 0.5 + d_r / (2.0 * c.G * c.d_h)}
+        if gqa_us:
+            row["time_ratio_gva_over_gqa"] = us / gqa_us
+        rows.append(row)
+        del pools, y, g, qa, ws
+        torch.cuda.empty_cache()
+    return {"shape": f"B={cfg.B} H={cfg.H} G={cfg.G} d_h={cfg.d_h} T={cfg.T}",
+            "gqa_us_avg_same_shape": gqa_us, "rows": rows}
 
 
 def bench_multi(torch, gva, syn, cfg, dev, steps, warmup, L):
@@ -668,6 +738,19 @@ def bench_gqa(torch, gva, syn, cfg, dev, steps, warmup):
     return {"us_avg": avg * 1e3, "cache_bytes": byts, "GBps": byts / (avg * 1e-3) / 1e9}
 
 
+def cpu_model_name():
+    """The host CPU's model name (the lscpu 'Model name' line, read from
+    /proc/cpuinfo), or None where it cannot be read."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg, x, target_s):
     """The float64 oracle on the host: whole sequences of the same workload,
     as many as fit the time target, scaled to cache GB/s."""
@@ -695,6 +778,7 @@ def cpu_baseline(cfg, x, target_s):
         seqs += 1
     gbs = done_tokens * per_tok / spent / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model_name(), "host_cpus": os.cpu_count(),
             "sample": f"{seqs} whole sequences ({done_tokens} context tokens x {cfg.H} heads)"
                       f" of {cfg.name}, float64, keys materialised, {spent:.1f} s",
             "queries_ctx_per_s": done_tokens / spent}

@@ -14,8 +14,8 @@ import torch
 
 import oracle as o
 import synthetic as syn
-from parity_util import (announce, assert_bf16_parity, assert_fp32_parity, cpu,
-                         seq_subpool)
+from parity_util import (announce, assert_bf16_parity, assert_bf16_split_precision,
+                         assert_fp32_parity, cpu, seq_subpool)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,6 +84,7 @@ def _check_all(g, gpu, cfg, seqs=None, heads=None, **kw):
     sel = np.isfinite(ref_lse)
     got = cpu(out).double().numpy()
     assert_bf16_parity(got[sel], ref_out[sel], what=cfg.name + " out")
+    assert_bf16_split_precision(got[sel], ref_out[sel], what=cfg.name + " out")
     np.testing.assert_allclose(cpu(lse).double().numpy()[sel], ref_lse[sel],
                                rtol=0, atol=1e-3)
     return x, h, out
@@ -129,12 +130,14 @@ def test_large_model_sampled(g, gpu):
             sub["block_table"], sub["seq_lens"], base=cfg.rope_base, heads=[hh])
         assert_bf16_parity(cpu(out[b, hh]).double().numpy(), ref[0, hh],
                            what=f"large_model b={b} h={hh}")
+        assert_bf16_split_precision(cpu(out[b, hh]).double().numpy(), ref[0, hh],
+                                    what=f"large_model b={b} h={hh}")
         assert abs(float(lse[b, hh]) - ref_lse[0, hh]) < 1e-3
 
 
 # ----------------------------------------------------------- edge cases ----
 
-EDGE_LENS = [1, 2, 63, 64, 65, 127, 128, 129, 1000]
+EDGE_LENS = [1, 2, 15, 16, 17, 31, 33, 63, 64, 65, 127, 128, 129, 1000]
 
 
 @pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
@@ -396,6 +399,44 @@ def test_decode_step_matches_oracle_and_separate_calls(g, gpu, name, kw):
         assert_fp32_parity(cpu(out), ref)
     else:
         assert_bf16_parity(cpu(out).double().numpy(), ref)
+        assert_bf16_split_precision(cpu(out).double().numpy(), ref)
+
+
+def test_decode_step_at_the_benchmark_configuration(g, gpu):
+    """The call the benchmark times, at its sizes: gva_decode_step with the
+    append on the 350M-shaped workload (B = 32, T = 4096), its workspace
+    zero-filled once and reused, against the oracle over every sequence and
+    head, on two calls in a row (the second starts from the counters the
+    first left)."""
+    cfg = syn.with_overrides(syn.get_config("decode_350m"), append=True)
+    announce("decode_step at the benchmark configuration", cfg.B, cfg.T)
+    x, h = gen(cfg, gpu)
+    ws = torch.zeros(g.decode_step_workspace_bytes(x["q_nope"], x["q_rope"], x["v_pool"],
+                                                   x["k_pool"], x["block_table"],
+                                                   x["max_seq_len"]),
+                     dtype=torch.uint8, device=gpu)
+    vp, kp = oracle_pools(h, cfg)
+    ref, ref_lse = o.gva_decode_materialized(
+        h["q_nope"], h["q_rope"], h["M"], vp, kp, h["block_table"], h["seq_lens"],
+        base=cfg.rope_base)
+    first = None
+    for call in range(2):
+        out = torch.full((cfg.B, cfg.H, cfg.d_h), float("nan"), device=gpu)
+        lse = torch.full((cfg.B, cfg.H), float("nan"), device=gpu)
+        g.decode_step(x["q_nope"], x["q_rope"], x["M"], x["v_pool"], x["k_pool"],
+                      x["block_table"], x["seq_lens"], x["max_seq_len"], v_new=x["v_new"],
+                      k_new=x["k_new"], rope_base=cfg.rope_base, workspace=ws, out=out,
+                      lse=lse)
+        torch.cuda.synchronize()
+        got = cpu(out).double().numpy()
+        assert_bf16_parity(got, ref, what=f"call {call}")
+        assert_bf16_split_precision(got, ref, what=f"call {call}")
+        np.testing.assert_allclose(cpu(lse).double().numpy(), ref_lse, rtol=0, atol=1e-3)
+        if first is None:
+            first = out.clone()
+        else:
+            assert torch.equal(out, first)  # bitwise reproducible
+    assert int(ws[:4].view(torch.int32).item()) == 0  # counters left at zero
 
 
 def test_decode_step_without_append(g, gpu):
@@ -565,7 +606,12 @@ def test_multi_query_decode(g, gpu, H, G, d_h, d_n, d_r, dtype, L):
         assert_fp32_parity(cpu(lse), ref_lse)
     else:
         assert_bf16_parity(cpu(out).double().numpy(), ref)
+        assert_bf16_split_precision(cpu(out).double().numpy(), ref)
         np.testing.assert_allclose(cpu(lse).double().numpy(), ref_lse, rtol=0, atol=1e-3)
+        # these shapes run on the split matrix-core kernels (the blocked
+        # prefill kernel, the fallback, needs no workspace)
+        assert g.decode_workspace_bytes_multi(cfg.B, H, L, x["v_pool"], x["k_pool"],
+                                              x["block_table"], x["max_seq_len"]) > 0
 
 
 @pytest.mark.parametrize("L", [2, 4])
