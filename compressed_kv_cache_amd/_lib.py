@@ -20,7 +20,8 @@ GVA_F32 = 0
 GVA_BF16 = 1
 STATUS = {0: "GVA_OK", 1: "GVA_ERR_NULL", 2: "GVA_ERR_SHAPE",
           3: "GVA_ERR_UNSUPPORTED", 4: "GVA_ERR_ALIGN",
-          5: "GVA_ERR_WORKSPACE", 6: "GVA_ERR_HIP"}
+          5: "GVA_ERR_WORKSPACE", 6: "GVA_ERR_HIP", 7: "GVA_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 16 << 20  # GVA_NOALLOC_SCRATCH_BYTES
 
 _P = ctypes.c_void_p
 _SHAPE = ctypes.POINTER(GvaShape)
@@ -43,6 +44,8 @@ SIGNATURES = {
     "gva_decode_step_workspace_size": (_I32, [_SHAPE, _I32, ctypes.POINTER(_SIZE)]),
     "gva_decode_step": (_I32, [_SHAPE, _P, _P, _P, _F32, _F32, _P, _P, _P, _P, _P, _P, _I32,
                                _P, _SIZE, _P, _P, _P]),
+    "gva_decode_step_noalloc": (_I32, [_SHAPE, _P, _P, _P, _F32, _F32, _P, _P, _P, _P, _P,
+                                       _P, _I32, _P, _P, _P]),
     "gva_absorb_query_multi": (_I32, [_SHAPE, _I32, _P, _P, _P, _P, _F32, _F32, _P, _P]),
     "gva_append_cache_multi": (_I32, [_SHAPE, _I32, _P, _P, _P, _P, _F32, _P, _P, _P]),
     "gva_decode_workspace_size_multi": (_I32, [_SHAPE, _I32, _I32, ctypes.POINTER(_SIZE)]),

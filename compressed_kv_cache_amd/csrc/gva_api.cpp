@@ -238,6 +238,76 @@ gva_status decode(const gva_shape* shape, int32_t q_len, const float* q, float q
   return to_status(gva::launch_decode_ref(s, plan, a, strm));
 }
 
+// The step (append + absorb, then decode).  noalloc: the workspace is the
+// library's fixed scratch (looked up here, after every host check), and the
+// prologue clears the split counters the decode will use.
+gva_status step_impl(const gva_shape* shape, int32_t q_len, const float* q_nope,
+                     const float* q_rope, const float* M, float softmax_scale, float rope_base,
+                     const float* v_new, const float* k_new, void* v_pool, void* k_pool,
+                     const int32_t* block_table, const int32_t* seq_lens, int32_t max_seq_len,
+                     void* workspace, size_t workspace_bytes, float* out, float* lse,
+                     void* stream, bool noalloc) {
+  if (!shape) return GVA_ERR_NULL;
+  const gva_shape& s = *shape;
+  gva_status st = check_absorb_shape(s, softmax_scale, rope_base);
+  if (st != GVA_OK) return st;
+  st = check_decode_args(shape, max_seq_len, false, q_len);
+  if (st != GVA_OK) return st;
+  gva::DecodePlan plan;
+  const gva_shape sc = columns(s, q_len);
+  st = make_plan(sc, max_seq_len, false, q_len, &plan);
+  if (st != GVA_OK) return st;
+  if (s.B == 0) return GVA_OK;
+  if (!q_nope || (s.d_r > 0 && (!q_rope || !k_pool)) || !M || !v_pool || !block_table ||
+      !seq_lens || !out || (!workspace && !noalloc))
+    return GVA_ERR_NULL;
+  // append requested by v_new; its key part only when there is a positional slice
+  if ((v_new == nullptr && k_new != nullptr) || (v_new && s.d_r > 0 && !k_new))
+    return GVA_ERR_NULL;
+  if (!aligned16(v_pool) || !aligned16(k_pool) || !aligned16(out) ||
+      (!noalloc && !aligned16(workspace)))
+    return GVA_ERR_ALIGN;
+  const size_t qa_off = step_qa_offset(plan.workspace_bytes);
+  const size_t need = qa_off + step_qa_bytes(s, q_len);
+  if (noalloc) {
+    if (need > GVA_NOALLOC_SCRATCH_BYTES) return GVA_ERR_SCRATCH;
+    if (gva::noalloc_scratch(&workspace) != hipSuccess) return GVA_ERR_HIP;
+    workspace_bytes = GVA_NOALLOC_SCRATCH_BYTES;
+  }
+  if (workspace_bytes < need) return GVA_ERR_WORKSPACE;
+  float* qa = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + qa_off);
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  // append (optional) + absorb in one launch; the last new token and the
+  // last query sit at position seq_lens[b] - 1
+  // (noalloc: the split counters are cleared in the same launch)
+  const int n_counters =
+      noalloc ? static_cast<int>(plan.ticket_bytes / (gva::kTicketStride * 4)) : 0;
+  hipError_t e = gva::launch_prologue(s, q_nope, q_rope, M, absorb_scale(s, softmax_scale), qa,
+                                      v_new, k_new, block_table, v_pool, k_pool, seq_lens, -1,
+                                      q_len, rope_base, strm,
+                                      static_cast<unsigned*>(workspace), n_counters);
+  if (e != hipSuccess) return GVA_ERR_HIP;
+  gva::DecodeArgs a{};
+  a.q = qa;
+  a.v_pool = v_pool;
+  a.k_pool = k_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.max_seq_len = max_seq_len;
+  a.tickets = static_cast<unsigned*>(workspace);
+  a.partials = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + plan.ticket_bytes);
+  a.out = out;
+  a.lse = lse;
+  a.q_scale = 1.0f;
+  a.q_len = q_len;
+  a.keys_separate = false;
+  if (plan.kernel == gva::kKernelPrefill)
+    return to_status(gva::launch_prefill(s, q_len, qa, v_pool, k_pool, block_table, seq_lens,
+                                         max_seq_len, false, 1.0f, out, lse, strm));
+  if (plan.kernel == gva::kKernelMfma) return to_status(gva::launch_decode_mfma(sc, plan, a, strm));
+  return to_status(gva::launch_decode_ref(sc, plan, a, strm));
+}
+
 // Ordinary RoPE on the reconstructed key: d_n is the key width d_k, no
 // separate positional slice (d_r = 0).
 gva_status check_rope_keys(const gva_shape* shape, int32_t max_seq_len, float softmax_scale,
@@ -271,6 +341,7 @@ const char* gva_status_string(int32_t status) {
     case GVA_ERR_ALIGN: return "pointer not 16-byte aligned";
     case GVA_ERR_WORKSPACE: return "workspace too small";
     case GVA_ERR_HIP: return "HIP runtime error";
+    case GVA_ERR_SCRATCH: return "needs more than the library's fixed device scratch";
     default: return "unknown status";
   }
 }
@@ -393,54 +464,20 @@ gva_status gva_decode_step_multi(const gva_shape* shape, int32_t q_len, const fl
                                  const int32_t* seq_lens, int32_t max_seq_len, void* workspace,
                                  size_t workspace_bytes, float* out, float* lse,
                                  void* stream) {
-  if (!shape) return GVA_ERR_NULL;
-  const gva_shape& s = *shape;
-  gva_status st = check_absorb_shape(s, softmax_scale, rope_base);
-  if (st != GVA_OK) return st;
-  st = check_decode_args(shape, max_seq_len, false, q_len);
-  if (st != GVA_OK) return st;
-  gva::DecodePlan plan;
-  const gva_shape sc = columns(s, q_len);
-  st = make_plan(sc, max_seq_len, false, q_len, &plan);
-  if (st != GVA_OK) return st;
-  if (s.B == 0) return GVA_OK;
-  if (!q_nope || (s.d_r > 0 && (!q_rope || !k_pool)) || !M || !v_pool || !block_table ||
-      !seq_lens || !out || !workspace)
-    return GVA_ERR_NULL;
-  // append requested by v_new; its key part only when there is a positional slice
-  if ((v_new == nullptr && k_new != nullptr) || (v_new && s.d_r > 0 && !k_new))
-    return GVA_ERR_NULL;
-  if (!aligned16(v_pool) || !aligned16(k_pool) || !aligned16(out) || !aligned16(workspace))
-    return GVA_ERR_ALIGN;
-  const size_t qa_off = step_qa_offset(plan.workspace_bytes);
-  if (workspace_bytes < qa_off + step_qa_bytes(s, q_len)) return GVA_ERR_WORKSPACE;
-  float* qa = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + qa_off);
-  hipStream_t strm = static_cast<hipStream_t>(stream);
-  // append (optional) + absorb in one launch; the last new token and the
-  // last query sit at position seq_lens[b] - 1
-  hipError_t e = gva::launch_prologue(s, q_nope, q_rope, M, absorb_scale(s, softmax_scale), qa,
-                                      v_new, k_new, block_table, v_pool, k_pool, seq_lens, -1,
-                                      q_len, rope_base, strm);
-  if (e != hipSuccess) return GVA_ERR_HIP;
-  gva::DecodeArgs a{};
-  a.q = qa;
-  a.v_pool = v_pool;
-  a.k_pool = k_pool;
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
-  a.max_seq_len = max_seq_len;
-  a.tickets = static_cast<unsigned*>(workspace);
-  a.partials = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + plan.ticket_bytes);
-  a.out = out;
-  a.lse = lse;
-  a.q_scale = 1.0f;
-  a.q_len = q_len;
-  a.keys_separate = false;
-  if (plan.kernel == gva::kKernelPrefill)
-    return to_status(gva::launch_prefill(s, q_len, qa, v_pool, k_pool, block_table, seq_lens,
-                                         max_seq_len, false, 1.0f, out, lse, strm));
-  if (plan.kernel == gva::kKernelMfma) return to_status(gva::launch_decode_mfma(sc, plan, a, strm));
-  return to_status(gva::launch_decode_ref(sc, plan, a, strm));
+  return step_impl(shape, q_len, q_nope, q_rope, M, softmax_scale, rope_base, v_new, k_new,
+                   v_pool, k_pool, block_table, seq_lens, max_seq_len, workspace,
+                   workspace_bytes, out, lse, stream, false);
+}
+
+gva_status gva_decode_step_noalloc(const gva_shape* shape, const float* q_nope,
+                                   const float* q_rope, const float* M, float softmax_scale,
+                                   float rope_base, const float* v_new, const float* k_new,
+                                   void* v_pool, void* k_pool, const int32_t* block_table,
+                                   const int32_t* seq_lens, int32_t max_seq_len, float* out,
+                                   float* lse, void* stream) {
+  return step_impl(shape, 1, q_nope, q_rope, M, softmax_scale, rope_base, v_new, k_new,
+                   v_pool, k_pool, block_table, seq_lens, max_seq_len, nullptr, 0, out, lse,
+                   stream, true);
 }
 
 gva_status gva_decode_step(const gva_shape* shape, const float* q_nope, const float* q_rope,

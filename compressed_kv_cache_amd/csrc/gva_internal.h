@@ -50,12 +50,19 @@ hipError_t launch_append(const gva_shape& s, int q_len, const float* v_new, cons
                          void* v_pool, void* k_pool, hipStream_t stream);
 
 // Absorption (q_nope != nullptr) and append (v_new != nullptr) in one launch;
-// the last token of sequence b sits at position pos[b] + pos_offset.
+// the last token of sequence b sits at position pos[b] + pos_offset.  With
+// clear_counters, the same launch also zeroes n_counters split counters
+// (kTicketStride apart) for the decode that follows it.
 hipError_t launch_prologue(const gva_shape& s, const float* q_nope, const float* q_rope,
                            const float* M, float scale, float* qa, const float* v_new,
                            const float* k_new, const int32_t* block_table, void* v_pool,
                            void* k_pool, const int32_t* pos, int pos_offset, int q_len,
-                           double base, hipStream_t stream);
+                           double base, hipStream_t stream, unsigned* clear_counters = nullptr,
+                           int n_counters = 0);
+
+// Device address of the current GPU's fixed scratch array
+// (GVA_NOALLOC_SCRATCH_BYTES), looked up once per device.
+hipError_t noalloc_scratch(void** addr);
 
 // GVA decode (keys_separate = false: the key of head h is [V_g(h) | k_rope],
 // query already scaled) and GQA decode (keys_separate = true: key K_g(h),

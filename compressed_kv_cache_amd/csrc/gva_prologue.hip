@@ -42,7 +42,10 @@ struct PrologueArgs {
   int q_len;           // tokens per sequence (L): token i sits at that position - (L-1) + i
   int B, H, G, d_h, d_n, d_r, bs, max_blocks, num_blocks;
   int absorb_blocks;   // blocks [0, absorb_blocks) absorb the content slice,
-  int rope_blocks;     // the next rope_blocks rotate the position slice, the rest append
+  int rope_blocks;     // the next rope_blocks rotate the position slice,
+  int append_blocks;   // the next append_blocks append, the rest clear counters
+  unsigned* counters;  // split counters to zero (kTicketStride apart)
+  int n_counters;
   int vec4;            // q_nope and M rows 16-byte aligned (d_n % 4 == 0)
 };
 
@@ -212,12 +215,17 @@ __device__ __forceinline__ void append_block(const PrologueArgs& a, const RopeTa
 template <typename CT>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a, RopeTable rt) {
   const int id = blockIdx.x;
-  if (id < a.absorb_blocks)
+  if (id < a.absorb_blocks) {
     absorb_block(a, id);
-  else if (id < a.absorb_blocks + a.rope_blocks)
+  } else if (id < a.absorb_blocks + a.rope_blocks) {
     rope_block(a, rt, id - a.absorb_blocks);
-  else
+  } else if (id < a.absorb_blocks + a.rope_blocks + a.append_blocks) {
     append_block<CT>(a, rt, id - a.absorb_blocks - a.rope_blocks);
+  } else {  // one split counter per thread
+    const int i = (id - a.absorb_blocks - a.rope_blocks - a.append_blocks) * kThreads +
+                  static_cast<int>(threadIdx.x);
+    if (i < a.n_counters) a.counters[static_cast<size_t>(i) * kTicketStride] = 0u;
+  }
 }
 
 RopeTable rope_table(int d_r, double base) {
@@ -233,8 +241,10 @@ hipError_t launch_prologue(const gva_shape& s, const float* q_nope, const float*
                            const float* M, float scale, float* qa, const float* v_new,
                            const float* k_new, const int32_t* block_table, void* v_pool,
                            void* k_pool, const int32_t* pos, int pos_offset, int q_len,
-                           double base, hipStream_t stream) {
-  if (s.d_h % 16 || s.d_r / 2 > kMaxHalfRope || s.d_r < 0 || s.d_r % 2 || q_len < 1)
+                           double base, hipStream_t stream, unsigned* clear_counters,
+                           int n_counters) {
+  if (s.d_h % 16 || s.d_r / 2 > kMaxHalfRope || s.d_r < 0 || s.d_r % 2 || q_len < 1 ||
+      n_counters < 0 || (n_counters > 0 && !clear_counters))
     return hipErrorInvalidValue;
   PrologueArgs a{};
   a.pos_offset = pos_offset;
@@ -266,8 +276,11 @@ hipError_t launch_prologue(const gva_shape& s, const float* q_nope, const float*
   const long long rope_items = q_nope ? rows * s.H * (s.d_r / 2) : 0;
   a.rope_blocks = static_cast<int>((rope_items + kThreads - 1) / kThreads);
   const long long append_items = v_new ? rows * (s.G * s.d_h / 4 + s.d_r / 2) : 0;
-  const int blocks = a.absorb_blocks + a.rope_blocks +
-                     static_cast<int>((append_items + kThreads - 1) / kThreads);
+  a.append_blocks = static_cast<int>((append_items + kThreads - 1) / kThreads);
+  a.counters = clear_counters;
+  a.n_counters = n_counters;
+  const int blocks = a.absorb_blocks + a.rope_blocks + a.append_blocks +
+                     (n_counters + kThreads - 1) / kThreads;
   if (blocks == 0) return hipSuccess;
   const RopeTable rt = rope_table(s.d_r, base);
   if (s.cache_dtype == GVA_BF16)

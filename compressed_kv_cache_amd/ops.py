@@ -285,6 +285,52 @@ def decode_step(q_nope, q_rope, M, v_pool, k_pool, block_table, seq_lens, max_se
     return out, lse
 
 
+def decode_step_noalloc(q_nope, q_rope, M, v_pool, k_pool, block_table, seq_lens,
+                        max_seq_len, v_new=None, k_new=None, softmax_scale=None,
+                        rope_base=10000.0, out=None, lse=None, want_lse=True):
+    """decode_step with no workspace argument (gva_decode_step_noalloc): the
+    library takes its workspace from a fixed device array of
+    NOALLOC_SCRATCH_BYTES per GPU.  `out` (and `lse`) are the caller's; pass
+    them to make the call allocate nothing at all.  Calls that overlap on
+    one GPU race."""
+    dev = v_pool.device
+    _need(q_nope, "q_nope", torch.float32, dev, 3)
+    _need(q_rope, "q_rope", torch.float32, dev, 3)
+    _need(M, "M", torch.float32, dev, 3)
+    _need(v_pool, "v_pool", v_pool.dtype, dev, 4)
+    _need(k_pool, "k_pool", v_pool.dtype, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    B, H, d_n = q_nope.shape
+    NB, bs, G, d_h = v_pool.shape
+    d_r = q_rope.shape[2]
+    if tuple(q_rope.shape[:2]) != (B, H) or tuple(M.shape) != (H, d_h, d_n) \
+            or tuple(k_pool.shape) != (NB, bs, d_r) or block_table.shape[0] != B \
+            or seq_lens.shape[0] != B:
+        raise ValueError("inconsistent shapes for decode_step_noalloc")
+    if (v_new is None) != (k_new is None):
+        raise ValueError("give both v_new and k_new, or neither")
+    if v_new is not None:
+        _need(v_new, "v_new", torch.float32, dev, 3)
+        _need(k_new, "k_new", torch.float32, dev, 2)
+        if tuple(v_new.shape) != (B, G, d_h) or tuple(k_new.shape) != (B, d_r):
+            raise ValueError("inconsistent shapes for v_new / k_new")
+    s = GvaShape(B, H, G, d_h, d_n, d_r, bs, block_table.shape[1], NB,
+                 _cache_dtype(v_pool, "v_pool"))
+    if out is None:
+        out = torch.empty((B, H, d_h), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    st = lib.gva_decode_step_noalloc(
+        ctypes.byref(s), _ptr(q_nope), _ptr(q_rope), _ptr(M), float(softmax_scale or 0.0),
+        float(rope_base), _ptr(v_new), _ptr(k_new), _ptr(v_pool), _ptr(k_pool),
+        _ptr(block_table), _ptr(seq_lens), int(max_seq_len), _ptr(out), _ptr(lse),
+        _stream(dev))
+    check("gva_decode_step_noalloc", st)
+    return out, lse
+
+
 # ---- several tokens per sequence (q_len = L): the *_multi entry points ----
 
 def absorb_query_multi(q_nope, q_rope, M, pos, softmax_scale=None, rope_base=10000.0,

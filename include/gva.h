@@ -22,8 +22,10 @@
  * Conventions shared by every entry point
  *   Memory    All tensor pointers are DEVICE pointers to dense row-major
  *             arrays, owned by the caller; the library allocates and frees
- *             nothing and keeps no state between calls.  Pointers to arrays
- *             read with vector loads (marked "16B") must be 16-byte aligned.
+ *             nothing and keeps no state between calls (the one exception
+ *             is the fixed device scratch of gva_decode_step_noalloc).
+ *             Pointers to arrays read with vector loads (marked "16B") must
+ *             be 16-byte aligned.
  *   Streams   Every call only enqueues work on `stream` and returns; results
  *             are ready when the stream reaches that point.
  *   Errors    Argument errors are detected on the host before any HIP call
@@ -56,7 +58,7 @@
 extern "C" {
 #endif
 
-#define GVA_ABI_VERSION 2
+#define GVA_ABI_VERSION 3
 
 typedef enum gva_status {
   GVA_OK = 0,
@@ -65,7 +67,9 @@ typedef enum gva_status {
   GVA_ERR_UNSUPPORTED = 3, /* valid sizes the library has no kernel for    */
   GVA_ERR_ALIGN = 4,       /* a 16B pointer is not 16-byte aligned          */
   GVA_ERR_WORKSPACE = 5,   /* workspace smaller than the size query returns */
-  GVA_ERR_HIP = 6          /* the HIP runtime rejected a launch             */
+  GVA_ERR_HIP = 6,         /* the HIP runtime rejected a launch             */
+  GVA_ERR_SCRATCH = 7      /* needs more than the library's fixed device
+                              scratch (gva_decode_step_noalloc only)        */
 } gva_status;
 
 typedef enum gva_dtype {
@@ -220,6 +224,32 @@ gva_status gva_decode_step(const gva_shape* shape, const float* q_nope,
                            int32_t max_seq_len, void* workspace,
                            size_t workspace_bytes, float* out, float* lse,
                            void* stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * step as gva_decode_step (same kernels, bit-identical results), with the
+ * workspace taken from a fixed device array inside the library instead of
+ * a caller's buffer: GVA_NOALLOC_SCRATCH_BYTES per GPU, reserved when the
+ * library's code is loaded on that GPU and held until the process ends.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); its first call on a device looks up that device's copy of the
+ * array (hipGetSymbolAddress), so make the first call outside graph
+ * capture.  Every call clears the split counters it uses (in its first
+ * launch), so no earlier call's contents matter.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (concurrent streams, threads) race and must be serialised by the
+ * caller.  A call whose workspace (gva_decode_step_workspace_size) exceeds
+ * GVA_NOALLOC_SCRATCH_BYTES returns GVA_ERR_SCRATCH before any HIP call.
+ * Other arguments, layouts and errors as gva_decode_step. */
+#define GVA_NOALLOC_SCRATCH_BYTES (16u << 20)
+gva_status gva_decode_step_noalloc(const gva_shape* shape, const float* q_nope,
+                                   const float* q_rope, const float* M,
+                                   float softmax_scale, float rope_base,
+                                   const float* v_new, const float* k_new,
+                                   void* v_pool, void* k_pool,
+                                   const int32_t* block_table,
+                                   const int32_t* seq_lens, int32_t max_seq_len,
+                                   float* out, float* lse, void* stream);
 
 /* Several tokens per sequence (q_len = L, 1 <= L <= 65536): the entry points
  * above with one more size.  Each query token is absorbed on its own, once

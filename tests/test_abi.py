@@ -50,8 +50,8 @@ def test_library_exports_every_declared_symbol(g):
 
 
 def test_version_and_status_strings(g):
-    assert g.lib.gva_abi_version() == 2
-    for code in range(7):
+    assert g.lib.gva_abi_version() == 3
+    for code in range(8):
         assert g.lib.gva_status_string(code)
     assert g.lib.gva_status_string(99) == b"unknown status"
 
@@ -327,3 +327,45 @@ def test_stream_read_probe_validation(g):
     from compressed_kv_cache_amd._lib import PROBE_BLOCKS
     assert PROBE_BLOCKS == int(re.search(r"#define GVA_PROBE_BLOCKS (\d+)",
                                          open(HEADER).read()).group(1))
+
+
+def _step_noalloc(g, s, ptrs, max_seq_len=128):
+    P = ctypes.c_void_p
+    return g.lib.gva_decode_step_noalloc(
+        ctypes.byref(s), P(ptrs.get("qn")), P(ptrs.get("qr")), P(ptrs.get("M")), 0.0,
+        10000.0, P(ptrs.get("vn")), P(ptrs.get("kn")), P(ptrs.get("v")), P(ptrs.get("k")),
+        P(ptrs.get("bt")), P(ptrs.get("sl")), max_seq_len, P(ptrs.get("out")),
+        P(ptrs.get("lse")), None)
+
+
+NOALLOC_GOOD = dict(qn=0x10000, qr=0x20000, M=0x30000, v=0x40000, k=0x50000, bt=0x60000,
+                    sl=0x70000, out=0x80000, lse=0x90000)
+
+
+@pytest.mark.parametrize("missing", ["qn", "qr", "M", "v", "k", "bt", "sl", "out"])
+def test_noalloc_step_null_pointers(g, missing):
+    ptrs = dict(NOALLOC_GOOD)
+    ptrs[missing] = None
+    assert _step_noalloc(g, _shape(g), ptrs) == 1
+
+
+def test_noalloc_step_rejects_a_workspace_past_the_scratch(g):
+    """A call whose step workspace exceeds the fixed device scratch is
+    refused with GVA_ERR_SCRATCH before any HIP call (fake pointers)."""
+    s = _shape(g, B=4096, max_blocks=64, num_blocks=4096 * 64)
+    n = ctypes.c_size_t(0)
+    assert g.lib.gva_decode_step_workspace_size(ctypes.byref(s), 4096, ctypes.byref(n)) == 0
+    assert n.value > g.NOALLOC_SCRATCH_BYTES
+    assert _step_noalloc(g, s, NOALLOC_GOOD, max_seq_len=4096) == 7
+    small = _shape(g, B=2)
+    assert g.lib.gva_decode_step_workspace_size(ctypes.byref(small), 128,
+                                                ctypes.byref(n)) == 0
+    assert n.value <= g.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_step_validates_like_the_step(g):
+    ptrs = dict(NOALLOC_GOOD)
+    ptrs["v"] = 0x40008  # misaligned cache
+    assert _step_noalloc(g, _shape(g), ptrs) == 4
+    assert _step_noalloc(g, _shape(g, H=15), NOALLOC_GOOD) == 2
+    assert _step_noalloc(g, _shape(g), NOALLOC_GOOD, max_seq_len=257) == 2
