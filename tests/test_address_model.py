@@ -147,7 +147,13 @@ def decode_reads(lens, bt, nb, G, DH, DR, cols, gqa=False, q_len=1, max_seq_len=
     B, max_blocks = bt.shape
     if max_seq_len is None:
         max_seq_len = int(max(max(lens), 0))
+    def valid(n):
+        n = int(n)
+        bad = n < 0 or n > max_seq_len or n > max_blocks * KB or (0 < n < q_len)
+        return 0 if bad else n
     chunk, num_chunks = plan_mfma(B, max_seq_len)
+    blocks = [(b, c) for b in range(B) for c in range(num_chunks)]
+    assert chunk % TILE == 0
     nht = cols // 16
     nsub = NW // nht
     vrow_bytes = G * DH * 2
@@ -161,35 +167,30 @@ def decode_reads(lens, bt, nb, G, DH, DR, cols, gqa=False, q_len=1, max_seq_len=
         d = min(16 * s + 4 * q4, DR - 4)     # positional-key dims, clamped into the row
         assert 0 <= d and 2 * d + 8 <= 2 * DR
     checked = 0
-    for b in range(B):
-        length = int(lens[b])
-        bad = (length < 0 or length > max_seq_len or length > max_blocks * KB
-               or (0 < length < q_len))
-        if bad:
-            length = 0
-        for c in range(num_chunks):
-            j_begin = c * chunk
-            active = j_begin < length
-            j_end = min(length, j_begin + chunk)
-            n_tiles = -(-(j_end - j_begin) // TILE) if active else 0
-            for wave in range(NW):
-                sub = wave >> (nht.bit_length() - 1)
-                n_my = -(-(n_tiles - sub) // nsub) if sub < n_tiles else 0
-                for i in loaded_tiles(n_my, NSET):
-                    k = sub + i * nsub
-                    idx = min((j_begin + TILE * k) // KB, max_blocks - 1)
-                    assert 0 <= idx < max_blocks
-                    blk = int(bt[b, idx])
-                    real = k < n_tiles
-                    in_pool = 0 <= blk < nb
-                    j0 = j_begin + TILE * k
-                    row0 = blk * KB + (j0 % KB) if (real and in_pool) else 0
-                    if not redirect:
-                        row0 = blk * KB + (j0 % KB)
-                    assert 0 <= row0 and row0 + max_r < pool_rows, (b, c, wave, k, blk)
-                    if not gqa and DR > 0:
-                        assert row0 + (TILE - 1) < pool_rows  # k_rope rows row0 + li
-                    checked += 1
+    for b, c in blocks:
+        length = valid(lens[b])
+        j_begin = c * chunk
+        active = j_begin < length
+        j_end = min(length, j_begin + chunk)
+        n_tiles = -(-(j_end - j_begin) // TILE) if active else 0
+        for wave in range(NW):
+            sub = wave >> (nht.bit_length() - 1)
+            n_my = -(-(n_tiles - sub) // nsub) if sub < n_tiles else 0
+            for i in loaded_tiles(n_my, NSET):
+                k = sub + i * nsub
+                idx = min((j_begin + TILE * k) // KB, max_blocks - 1)
+                assert 0 <= idx < max_blocks
+                blk = int(bt[b, idx])
+                real = k < n_tiles
+                in_pool = 0 <= blk < nb
+                j0 = j_begin + TILE * k
+                row0 = blk * KB + (j0 % KB) if (real and in_pool) else 0
+                if not redirect:
+                    row0 = blk * KB + (j0 % KB)
+                assert 0 <= row0 and row0 + max_r < pool_rows, (b, c, wave, k, blk)
+                if not gqa and DR > 0:
+                    assert row0 + (TILE - 1) < pool_rows  # k_rope rows row0 + li
+                checked += 1
     return checked
 
 
