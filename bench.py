@@ -76,6 +76,8 @@ def parse():
                     help="skip the plain-read rate of the same cache buffers")
     ap.add_argument("--no-dr-sweep", action="store_true",
                     help="skip the decode timed over positional widths d_r = 0, 16, 24, 32")
+    ap.add_argument("--no-vector-scores", action="store_true",
+                    help="skip the decode timed with its scores on the vector units")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--ingest-counters", nargs=4, metavar="DIR")
@@ -355,6 +357,8 @@ def main():
         pools = None
         extra["dr_sweep"] = bench_dr_sweep(torch, gva, syn, cfg0, dev, args.steps,
                                            extra.get("gqa", {}).get("us_avg"))
+    if not args.no_vector_scores and cfg.cache_dtype == "bfloat16" and cfg.H == 4 * cfg.G:
+        extra["vector_scores"] = bench_vector_scores(torch, gva, syn, cfg0, dev, args.steps)
     if not args.no_multi:
         del pools
         torch.cuda.empty_cache()
@@ -460,6 +464,51 @@ def bench_read_probe(torch, gva, v_pools, dev, steps):
     return res
 
 
+def time_decode(torch, gva, c, y, dev, steps):
+    """Average decode time (us) at config c with inputs y: graphs over
+    rotating cache copies (at least 1 GiB, so no launch reads from L2 or
+    the last-level cache what an earlier one left there), HIP events on the
+    launch stream."""
+    pool_bytes = (y["v_pool"].numel() + y["k_pool"].numel()) * y["v_pool"].element_size()
+    R = max(1, math.ceil(ROTATE_BYTES / pool_bytes))
+    pools = [(y["v_pool"], y["k_pool"])] + [
+        (y["v_pool"].clone(), y["k_pool"].clone()) for _ in range(R - 1)]
+    qa = gva.absorb_query(y["q_nope"], y["q_rope"], y["M"], y["pos"], rope_base=c.rope_base)
+    ws = torch.zeros(max(16, gva.decode_workspace_bytes(
+        c.B, c.H, y["v_pool"], y["k_pool"], y["block_table"], y["max_seq_len"])),
+        dtype=torch.uint8, device=dev)
+    out = torch.empty((c.B, c.H, c.d_h), dtype=torch.float32, device=dev)
+    lse = torch.empty((c.B, c.H), dtype=torch.float32, device=dev)
+
+    def launch(i):
+        vp, kp = pools[i % R]
+        gva.decode_attention(qa, vp, kp, y["block_table"], y["seq_lens"],
+                             y["max_seq_len"], workspace=ws, out=out, lse=lse)
+
+    S = max(R, 8)
+    for i in range(S):
+        launch(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(S):
+            launch(i)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(2, -(-steps // S))
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) / (reps * S) * 1e3
+    del pools, g, qa, ws
+    torch.cuda.empty_cache()
+    return us
+
+
 def bench_dr_sweep(torch, gva, syn, cfg, dev, steps, gqa_us):
     """The decode at one shape over positional widths d_r (d_n = d_h - d_r),
     same protocol as the headline decode (graphs over rotating cache copies,
@@ -473,42 +522,7 @@ def bench_dr_sweep(torch, gva, syn, cfg, dev, steps, gqa_us):
         y = syn.make_gva_inputs(c, device=dev)
         tokens = int(y["seq_lens_host"].sum())
         byts = tokens * (c.G * c.d_h + c.d_r) * 2
-        pool_bytes = (y["v_pool"].numel() + y["k_pool"].numel()) * 2
-        R = max(1, math.ceil(ROTATE_BYTES / pool_bytes))
-        pools = [(y["v_pool"], y["k_pool"])] + [
-            (y["v_pool"].clone(), y["k_pool"].clone()) for _ in range(R - 1)]
-        qa = gva.absorb_query(y["q_nope"], y["q_rope"], y["M"], y["pos"],
-                              rope_base=c.rope_base)
-        ws = torch.zeros(max(16, gva.decode_workspace_bytes(
-            c.B, c.H, y["v_pool"], y["k_pool"], y["block_table"], y["max_seq_len"])),
-            dtype=torch.uint8, device=dev)
-        out = torch.empty((c.B, c.H, c.d_h), dtype=torch.float32, device=dev)
-        lse = torch.empty((c.B, c.H), dtype=torch.float32, device=dev)
-
-        def launch(i):
-            vp, kp = pools[i % R]
-            gva.decode_attention(qa, vp, kp, y["block_table"], y["seq_lens"],
-                                 y["max_seq_len"], workspace=ws, out=out, lse=lse)
-
-        S = max(R, 8)
-        for i in range(S):
-            launch(i)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(S):
-                launch(i)
-        g.replay()
-        torch.cuda.synchronize()
-        reps = max(2, -(-steps // S))
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(reps):
-            g.replay()
-        t1.record()
-        torch.cuda.synchronize()
-        us = t0.elapsed_time(t1) / (reps * S) * 1e3
+        us = time_decode(torch, gva, c, y, dev, steps)
         row = {"d_r": d_r, "d_n": c.d_n, "us_avg": us, "cache_bytes": byts,
                "GBps": byts / (us * 1e-6) / 1e9,
                "frac_of_peak": byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
@@ -516,10 +530,36 @@ def bench_dr_sweep(torch, gva, syn, cfg, dev, steps, gqa_us):
         if gqa_us:
             row["time_ratio_gva_over_gqa"] = us / gqa_us
         rows.append(row)
-        del pools, y, g, qa, ws
+        del y
         torch.cuda.empty_cache()
     return {"shape": f"B={cfg.B} H={cfg.H} G={cfg.G} d_h={cfg.d_h} T={cfg.T}",
             "gqa_us_avg_same_shape": gqa_us, "rows": rows}
+
+
+def bench_vector_scores(torch, gva, syn, cfg, dev, steps):
+    """The decode with its scores on the vector units (GVA_DECODE_VALU=1:
+    v_dot2_f32_bf16 over the same bf16 high and low query parts, the same
+    streaming, staging, P.V and merge) beside the matrix-core decode, at the
+    workload's shape, same protocol as the headline decode."""
+    y = syn.make_gva_inputs(cfg, device=dev)
+    tokens = int(y["seq_lens_host"].sum())
+    byts = tokens * (cfg.G * cfg.d_h + cfg.d_r) * 2
+    res = {"shape": f"B={cfg.B} H={cfg.H} G={cfg.G} d_h={cfg.d_h} d_r={cfg.d_r} T={cfg.T}",
+           "cache_bytes": byts}
+    for name, flag in (("matrix_scores", None), ("vector_scores", "1")):
+        if flag:
+            os.environ["GVA_DECODE_VALU"] = flag
+        try:
+            us = time_decode(torch, gva, cfg, y, dev, steps)
+        finally:
+            os.environ.pop("GVA_DECODE_VALU", None)
+        res[name] = {"us_avg": us, "GBps": byts / (us * 1e-6) / 1e9,
+                     "frac_of_peak": byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    res["time_ratio_vector_over_matrix"] = (res["vector_scores"]["us_avg"] /
+                                            res["matrix_scores"]["us_avg"])
+    del y
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_multi(torch, gva, syn, cfg, dev, steps, warmup, L):

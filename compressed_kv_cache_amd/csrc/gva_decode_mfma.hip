@@ -43,6 +43,7 @@ namespace gva {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -259,11 +260,92 @@ __device__ __forceinline__ void load_tile(const WaveCtx& w, int k, int n_tiles,
 // (GVA: copied first, and the score operands read back from LDS).  Rows
 // past the sequence end carry whatever the slot holds: the caller masks
 // their scores, and their LDS copy is zero.
+// The same scores on the vector units (the matrix-core ablation; not the
+// library's default path): v_dot2_f32_bf16 over the same bf16 high and low
+// query parts.  Lane (q4, li) forms, for all 16 tokens of the tile, the
+// partial dot over its quarter of head li's dims (content dims 32 s + 8 q4
+// .. +7 of its group, position dims 16 s + 4 q4 .. +3), and a two-step
+// exchange across the four lanes of the head (xor 32, then xor 16) leaves it
+// the totals of tokens 4 q4 .. +3: the layout the matrix instruction gives.
+__device__ __forceinline__ float dot2bf(unsigned a, unsigned b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
 template <int GT, int DH, int DR, bool GQA>
+__device__ __forceinline__ f32x4 score_and_stage_valu(const WaveCtx& w, int cnt,
+                                                      const TileRegs<GT, DH, DR, GQA>& t,
+                                                      const QOps<GT, DH, DR, GQA>& qo,
+                                                      int half) {
+  using C = Cfg<GT, DH, DR, GQA>;
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  wave_lds_fence();
+#pragma unroll
+  for (int x = 0; x < C::NV; ++x) {
+    const int r = w.lrow + piece_row<C::ROWB>(x);
+    const int c = w.lchunk + piece_chunk<C::ROWB>(x);
+    *reinterpret_cast<u32x4*>(w.lds + lds_off(16 * half + r, c, C::ROWB)) =
+        r < cnt ? t.v[x] : z4;
+  }
+  wave_lds_fence();
+  float part[16];
+#pragma unroll
+  for (int tok = 0; tok < 16; ++tok) {
+    float acc = 0.f;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      const int chunk = w.lg * (DH / 8) + 4 * s + w.q4;
+      const u32x4 v =
+          *reinterpret_cast<const u32x4*>(w.lds + lds_off(16 * half + tok, chunk, C::ROWB));
+      const u32x4 qh = __builtin_bit_cast(u32x4, qo.qh[s]);
+      const u32x4 ql = __builtin_bit_cast(u32x4, qo.ql[s]);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        acc = dot2bf(v[p], qh[p], acc);
+        acc = dot2bf(v[p], ql[p], acc);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < C::NR; ++s) {
+      // token tok's position dims 16 s + 4 q4 .. +3 sit in lane tok + 16 q4
+      const int src = tok + 16 * w.q4;
+      const unsigned r0 = __shfl(t.r[s][0], src, 64), r1 = __shfl(t.r[s][1], src, 64);
+      const u32x2 rh = __builtin_bit_cast(u32x2, qo.rh[s]);
+      const u32x2 rl = __builtin_bit_cast(u32x2, qo.rl[s]);
+      acc = dot2bf(r0, rh[0], acc);
+      acc = dot2bf(r0, rl[0], acc);
+      acc = dot2bf(r1, rh[1], acc);
+      acc = dot2bf(r1, rl[1], acc);
+    }
+    part[tok] = acc;
+  }
+  // keep tokens 8 h1 .. +7 (h1 = q4 >> 1), add the partner's (xor 32)
+  const bool h1 = (w.q4 >> 1) != 0;
+  float keep[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float mine = h1 ? part[8 + i] : part[i];
+    const float other = h1 ? part[i] : part[8 + i];
+    keep[i] = mine + __shfl_xor(other, 32, 64);
+  }
+  // keep tokens 4 q4 .. +3, add the partner's (xor 16)
+  const bool h0 = (w.q4 & 1) != 0;
+  f32x4 sc;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float mine = h0 ? keep[4 + r] : keep[r];
+    const float other = h0 ? keep[r] : keep[4 + r];
+    sc[r] = mine + __shfl_xor(other, 16, 64);
+  }
+  return sc;
+}
+
+template <bool VALU, int GT, int DH, int DR, bool GQA>
 __device__ __forceinline__ f32x4 score_and_stage(const WaveCtx& w, int cnt,
                                                  const TileRegs<GT, DH, DR, GQA>& t,
                                                  const QOps<GT, DH, DR, GQA>& qo, int half) {
   using C = Cfg<GT, DH, DR, GQA>;
+  if constexpr (VALU && !GQA) return score_and_stage_valu(w, cnt, t, qo, half);
   const u32x4 z4 = {0u, 0u, 0u, 0u};
   f32x4 sg[GT];
   if constexpr (GQA) {
@@ -420,7 +502,7 @@ __device__ __forceinline__ int lane_count(const WaveCtx& w, int k) {
 // P.V update.  RELOAD_Y is a template flag: a branch around the reload
 // would make the compiler assume, at the loop head, that y has nothing in
 // flight, and wait there for every load.
-template <bool RELOAD_Y = true, int GT, int DH, int DR, bool GQA>
+template <bool RELOAD_Y = true, bool VALU = false, int GT, int DH, int DR, bool GQA>
 __device__ __forceinline__ void pair_step(const WaveCtx& w, const QOps<GT, DH, DR, GQA>& qo,
                                           SoftState<GT, DH, DR, GQA>& st, int n_tiles, int& bad,
                                           TileRegs<GT, DH, DR, GQA>& x,
@@ -428,33 +510,33 @@ __device__ __forceinline__ void pair_step(const WaveCtx& w, const QOps<GT, DH, D
                                           int ny) {
   const int cx = max(0, min(kTileTok, w.j_end - (w.j_begin + kTileTok * kx)));
   const int cy = max(0, min(kTileTok, w.j_end - (w.j_begin + kTileTok * ky)));
-  const f32x4 sa = score_and_stage(w, cx, x, qo, 0);
+  const f32x4 sa = score_and_stage<VALU>(w, cx, x, qo, 0);
   load_tile(w, nx, n_tiles, x, bad);
   // keep the scheduler from moving y's staging (which waits for y's data)
   // above x's reload: the reload must go out while y is still in flight
   __builtin_amdgcn_sched_barrier(0);
-  const f32x4 sb = score_and_stage(w, cy, y, qo, 1);
+  const f32x4 sb = score_and_stage<VALU>(w, cy, y, qo, 1);
   if constexpr (RELOAD_Y) load_tile(w, ny, n_tiles, y, bad);
   softmax_pv(w, lane_count(w, kx), lane_count(w, ky), sa, sb, st);
 }
 
 // The final step: no reloads.
-template <int GT, int DH, int DR, bool GQA>
+template <bool VALU = false, int GT, int DH, int DR, bool GQA>
 __device__ __forceinline__ void last_step(const WaveCtx& w, const QOps<GT, DH, DR, GQA>& qo,
                                           SoftState<GT, DH, DR, GQA>& st,
                                           const TileRegs<GT, DH, DR, GQA>& x,
                                           const TileRegs<GT, DH, DR, GQA>& y, int kx, int ky) {
   const int cx = max(0, min(kTileTok, w.j_end - (w.j_begin + kTileTok * kx)));
   const int cy = max(0, min(kTileTok, w.j_end - (w.j_begin + kTileTok * ky)));
-  const f32x4 sa = score_and_stage(w, cx, x, qo, 0);
-  const f32x4 sb = score_and_stage(w, cy, y, qo, 1);
+  const f32x4 sa = score_and_stage<VALU>(w, cx, x, qo, 0);
+  const f32x4 sb = score_and_stage<VALU>(w, cy, y, qo, 1);
   softmax_pv(w, lane_count(w, kx), lane_count(w, ky), sa, sb, st);
 }
 
 // NW: waves per block.  WPE: waves per SIMD the register budget is sized
 // for (2 where the tiles fit in 256 registers without spilling, else 1).
 // NSET: register tile sets in rotation (3, or 2 where three would spill).
-template <int GT, int DH, int DR, bool GQA, int NW, int WPE, int NSET>
+template <int GT, int DH, int DR, bool GQA, int NW, int WPE, int NSET, bool VALU = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void decode_mfma_kernel(
     const float* __restrict__ q, const bf16_t* __restrict__ v_pool,
@@ -610,18 +692,18 @@ void decode_mfma_kernel(
       load_tile_at(w, tile(2), n_tiles, blk_first[NSET - 1], tc, bad);
       int i = 0;
       for (int r = 0; r < n_steps / 3; ++r, i += 6) {
-        pair_step(w, qo, st, n_tiles, bad, ta, tb, tile(i), tile(i + 1), tile(i + 3), tile(i + 4));
-        pair_step(w, qo, st, n_tiles, bad, tc, ta, tile(i + 2), tile(i + 3), tile(i + 5),
+        pair_step<true, VALU>(w, qo, st, n_tiles, bad, ta, tb, tile(i), tile(i + 1), tile(i + 3), tile(i + 4));
+        pair_step<true, VALU>(w, qo, st, n_tiles, bad, tc, ta, tile(i + 2), tile(i + 3), tile(i + 5),
                   tile(i + 6));
-        pair_step(w, qo, st, n_tiles, bad, tb, tc, tile(i + 4), tile(i + 5), tile(i + 7),
+        pair_step<true, VALU>(w, qo, st, n_tiles, bad, tb, tc, tile(i + 4), tile(i + 5), tile(i + 7),
                   tile(i + 8));
       }
       const int rem = n_steps % 3;
       if (rem == 1) {
-        last_step(w, qo, st, ta, tb, tile(i), tile(i + 1));
+        last_step<VALU>(w, qo, st, ta, tb, tile(i), tile(i + 1));
       } else if (rem == 2) {
-        pair_step<false>(w, qo, st, n_tiles, bad, ta, tb, tile(i), tile(i + 1), tile(i + 3), 0);
-        last_step(w, qo, st, tc, ta, tile(i + 2), tile(i + 3));
+        pair_step<false, VALU>(w, qo, st, n_tiles, bad, ta, tb, tile(i), tile(i + 1), tile(i + 3), 0);
+        last_step<VALU>(w, qo, st, tc, ta, tile(i + 2), tile(i + 3));
       }
     } else {
       TileRegs<GT, DH, DR, GQA> ta, tb;
@@ -629,9 +711,9 @@ void decode_mfma_kernel(
       load_tile_at(w, tile(1), n_tiles, blk_first[1], tb, bad);
       int i = 0;
       for (; i < 2 * n_steps - 2; i += 2)
-        pair_step(w, qo, st, n_tiles, bad, ta, tb, tile(i), tile(i + 1), tile(i + 2),
+        pair_step<true, VALU>(w, qo, st, n_tiles, bad, ta, tb, tile(i), tile(i + 1), tile(i + 2),
                   tile(i + 3));
-      if (n_steps > 0) last_step(w, qo, st, ta, tb, tile(i), tile(i + 1));
+      if (n_steps > 0) last_step<VALU>(w, qo, st, ta, tb, tile(i), tile(i + 1));
     }
   }
 
@@ -823,13 +905,23 @@ void decode_mfma_kernel(
     __hip_atomic_store(seq_ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// GVA_DECODE_VALU=1 selects the vector-unit score instances (the
+// matrix-core ablation) where they exist: single-token GVA.
+bool valu_scores_requested() {
+  const char* v = getenv("GVA_DECODE_VALU");
+  return v && *v && atoi(v) != 0;
+}
+
 template <int GT, int DH, int DR, bool GQA, int NW, int WPE, int NSET>
 hipError_t launch_shape(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
                         hipStream_t stream) {
   dim3 grid(plan.num_chunks, s.B);
   if ((s.H / 16) > NW || NW % (s.H / 16) != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_mfma_kernel<GT, DH, DR, GQA, NW, WPE, NSET>), grid, dim3(64 * NW),
-                     0, stream,
+  auto kernel = decode_mfma_kernel<GT, DH, DR, GQA, NW, WPE, NSET, false>;
+  if constexpr (!GQA && GT == 4 && NSET == 2) {
+    if (valu_scores_requested()) kernel = decode_mfma_kernel<GT, DH, DR, GQA, NW, WPE, NSET, true>;
+  }
+  hipLaunchKernelGGL(kernel, grid, dim3(64 * NW), 0, stream,
                      a.q, static_cast<const bf16_t*>(a.v_pool),
                      static_cast<const bf16_t*>(a.k_pool), a.block_table, a.seq_lens,
                      a.max_seq_len, s.H, s.G, s.max_blocks, s.num_blocks, plan.chunk_tokens,

@@ -1001,3 +1001,27 @@ def test_stream_read_probe_checksum(g, gpu, nbytes):
     assert np.bitwise_xor.reduce(words) == want
     if nbytes == 0:
         assert not words.any()
+
+
+# ------------------------------------------- scores on the vector units ----
+# GVA_DECODE_VALU=1 runs the single-token GVA decode with its scores on the
+# vector units (v_dot2_f32_bf16 over the same bf16 high and low query parts),
+# the rest of the kernel unchanged: the matrix-core ablation.  It must meet
+# the same bars against the oracle.
+
+@pytest.mark.parametrize("name,kw", [
+    ("decode_350m", {}),
+    ("wide_rope_append", {"B": 16, "T": 3000}),                  # d_r = 24
+    ("decode_350m", {"B": 8, "T": 3000, "d_r": 0, "d_n": 64}),
+    ("decode_350m", {"B": 8, "T": 3000, "d_r": 32, "d_n": 32}),
+    ("decode_350m", {"B": len(EDGE_LENS), "T": None, "len_range": None}),
+    ("large_model", {"B": 3, "T": 2000, "with_gqa": False}),     # d_h = 128, d_r = 32
+])
+def test_vector_unit_scores(g, gpu, monkeypatch, name, kw):
+    cfg = syn.with_overrides(syn.get_config(name), **kw)
+    monkeypatch.setenv("GVA_DECODE_VALU", "1")
+    announce("vector-unit scores", name, kw)
+    extra = {}
+    if cfg.T is None and cfg.len_range is None:
+        extra = {"seq_lens": torch.tensor(EDGE_LENS, dtype=torch.int32), "shuffled": True}
+    _check_all(g, gpu, cfg, **extra)

@@ -240,7 +240,7 @@ def spill_sites(body):
 # value tiles (256 registers of tile data); it spills 44 bytes per lane.  It
 # is the same-shape comparison kernel, not a step of the method, and runs at
 # 84 % of the HBM peak on the larger-model shape despite the spill.
-KNOWN_SPILLS = ("decode_mfma_kernel<4, 128, 0, true, 4, 1, 2>",)
+KNOWN_SPILLS = ("decode_mfma_kernel<4, 128, 0, true, 4, 1, 2,",)
 
 
 def _demangled(name):
