@@ -340,6 +340,19 @@ def main():
         "gqa_cache_bytes_same_shape": tokens * 2 * cfg.G * cfg.d_h * esize,
     }
 
+    # the step's parts on their own (absorb: K1, append: K2, decode with its
+    # merge: K3 + K4), each timed as graphs of back-to-back calls
+    extra["per_call_us"] = {
+        "absorb_query": time_calls(torch, lambda i: gva.absorb_query(
+            x["q_nope"], x["q_rope"], x["M"], x["pos"], rope_base=cfg.rope_base, out=qa),
+            args.steps),
+        "append_cache": time_calls(torch, lambda i: gva.append_cache(
+            x["v_new"], x["k_new"], x["pos"], x["block_table"], pools[i % R][0],
+            pools[i % R][1], rope_base=cfg.rope_base), args.steps),
+        "decode_attention": dec_avg_ms * 1e3,
+        "decode_step": ms_per_step * 1e3,
+    }
+
     if not args.no_read_probe:
         extra["read_probe"] = bench_read_probe(torch, gva, [vp for vp, _ in pools], dev,
                                                args.steps)
@@ -462,6 +475,34 @@ def bench_read_probe(torch, gva, v_pools, dev, steps):
     del big
     torch.cuda.empty_cache()
     return res
+
+
+def time_calls(torch, call, steps, S=16):
+    """Average time (us) of call(i): graphs of S calls replayed back to back,
+    HIP events on the launch stream."""
+    for i in range(S):
+        call(i)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(0)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(S):
+            call(i)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(2, -(-steps // S))
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / (reps * S) * 1e3
 
 
 def time_decode(torch, gva, c, y, dev, steps):
