@@ -78,6 +78,8 @@ def parse():
                     help="skip the decode timed over positional widths d_r = 0, 16, 24, 32")
     ap.add_argument("--no-vector-scores", action="store_true",
                     help="skip the decode timed with its scores on the vector units")
+    ap.add_argument("--no-host-planned", action="store_true",
+                    help="skip the decode timed with its split planned from host lengths")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--ingest-counters", nargs=4, metavar="DIR")
@@ -372,6 +374,9 @@ def main():
                                            extra.get("gqa", {}).get("us_avg"))
     if not args.no_vector_scores and cfg.cache_dtype == "bfloat16" and cfg.H == 4 * cfg.G:
         extra["vector_scores"] = bench_vector_scores(torch, gva, syn, cfg0, dev, args.steps)
+    if (not args.no_host_planned and cfg.cache_dtype == "bfloat16" and cfg.H == 4 * cfg.G
+            and cfg.B <= 256):
+        extra["host_planned_split"] = bench_host_planned(torch, gva, syn, cfg0, dev, args.steps)
     if not args.no_multi:
         del pools
         torch.cuda.empty_cache()
@@ -505,26 +510,35 @@ def time_calls(torch, call, steps, S=16):
     return t0.elapsed_time(t1) / (reps * S) * 1e3
 
 
-def time_decode(torch, gva, c, y, dev, steps):
+def time_decode(torch, gva, c, y, dev, steps, lens_host=None):
     """Average decode time (us) at config c with inputs y: graphs over
     rotating cache copies (at least 1 GiB, so no launch reads from L2 or
     the last-level cache what an earlier one left there), HIP events on the
-    launch stream."""
+    launch stream.  lens_host: time gva_decode_attention_lens (the split
+    planned from these host lengths) instead."""
     pool_bytes = (y["v_pool"].numel() + y["k_pool"].numel()) * y["v_pool"].element_size()
     R = max(1, math.ceil(ROTATE_BYTES / pool_bytes))
     pools = [(y["v_pool"], y["k_pool"])] + [
         (y["v_pool"].clone(), y["k_pool"].clone()) for _ in range(R - 1)]
     qa = gva.absorb_query(y["q_nope"], y["q_rope"], y["M"], y["pos"], rope_base=c.rope_base)
-    ws = torch.zeros(max(16, gva.decode_workspace_bytes(
-        c.B, c.H, y["v_pool"], y["k_pool"], y["block_table"], y["max_seq_len"])),
-        dtype=torch.uint8, device=dev)
+    if lens_host is None:
+        wsb = gva.decode_workspace_bytes(c.B, c.H, y["v_pool"], y["k_pool"], y["block_table"],
+                                         y["max_seq_len"])
+    else:
+        wsb = gva.decode_workspace_bytes_lens(c.B, c.H, y["v_pool"], y["k_pool"],
+                                              y["block_table"])
+    ws = torch.zeros(max(16, wsb), dtype=torch.uint8, device=dev)
     out = torch.empty((c.B, c.H, c.d_h), dtype=torch.float32, device=dev)
     lse = torch.empty((c.B, c.H), dtype=torch.float32, device=dev)
 
     def launch(i):
         vp, kp = pools[i % R]
-        gva.decode_attention(qa, vp, kp, y["block_table"], y["seq_lens"],
-                             y["max_seq_len"], workspace=ws, out=out, lse=lse)
+        if lens_host is None:
+            gva.decode_attention(qa, vp, kp, y["block_table"], y["seq_lens"],
+                                 y["max_seq_len"], workspace=ws, out=out, lse=lse)
+        else:
+            gva.decode_attention_lens(qa, vp, kp, y["block_table"], y["seq_lens"], lens_host,
+                                      y["max_seq_len"], workspace=ws, out=out, lse=lse)
 
     S = max(R, 8)
     for i in range(S):
@@ -575,6 +589,26 @@ def bench_dr_sweep(torch, gva, syn, cfg, dev, steps, gqa_us):
         torch.cuda.empty_cache()
     return {"shape": f"B={cfg.B} H={cfg.H} G={cfg.G} d_h={cfg.d_h} T={cfg.T}",
             "gqa_us_avg_same_shape": gqa_us, "rows": rows}
+
+
+def bench_host_planned(torch, gva, syn, cfg, dev, steps):
+    """The decode with its split planned from the host copy of the lengths
+    (gva_decode_attention_lens) beside the split sized from max_seq_len, on
+    the workload's own lengths, same protocol as the headline decode."""
+    y = syn.make_gva_inputs(cfg, device=dev)
+    host = y["seq_lens_host"]
+    tokens = int(host.sum())
+    byts = tokens * (cfg.G * cfg.d_h + cfg.d_r) * 2
+    res = {"tokens": tokens, "max_len": int(host.max()), "cache_bytes": byts}
+    for name, lens in (("split_by_max_seq_len", None), ("host_planned", host)):
+        us = time_decode(torch, gva, cfg, y, dev, steps, lens)
+        res[name] = {"us_avg": us, "GBps": byts / (us * 1e-6) / 1e9,
+                     "frac_of_peak": byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    res["time_ratio_planned_over_max_len"] = (res["host_planned"]["us_avg"] /
+                                              res["split_by_max_seq_len"]["us_avg"])
+    del y
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_vector_scores(torch, gva, syn, cfg, dev, steps):

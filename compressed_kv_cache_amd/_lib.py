@@ -46,6 +46,12 @@ SIGNATURES = {
                                _P, _SIZE, _P, _P, _P]),
     "gva_decode_step_noalloc": (_I32, [_SHAPE, _P, _P, _P, _F32, _F32, _P, _P, _P, _P, _P,
                                        _P, _I32, _P, _P, _P]),
+    "gva_decode_workspace_size_lens": (_I32, [_SHAPE, ctypes.POINTER(_SIZE)]),
+    "gva_decode_attention_lens": (_I32, [_SHAPE, _P, _P, _P, _P, _P, _P, _I32, _P, _SIZE,
+                                         _P, _P, _P]),
+    "gva_decode_step_workspace_size_lens": (_I32, [_SHAPE, ctypes.POINTER(_SIZE)]),
+    "gva_decode_step_lens": (_I32, [_SHAPE, _P, _P, _P, _F32, _F32, _P, _P, _P, _P, _P, _P, _P,
+                                    _I32, _P, _SIZE, _P, _P, _P]),
     "gva_absorb_query_multi": (_I32, [_SHAPE, _I32, _P, _P, _P, _P, _F32, _F32, _P, _P]),
     "gva_append_cache_multi": (_I32, [_SHAPE, _I32, _P, _P, _P, _P, _F32, _P, _P, _P]),
     "gva_decode_workspace_size_multi": (_I32, [_SHAPE, _I32, _I32, ctypes.POINTER(_SIZE)]),

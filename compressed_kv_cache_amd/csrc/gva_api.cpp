@@ -13,6 +13,9 @@ hipError_t launch_decode_ref(const gva_shape& s, const DecodePlan& plan, const D
                              hipStream_t stream);
 bool mfma_decode_supported(const gva_shape& s, bool keys_separate, int q_len);
 DecodePlan plan_mfma_decode(const gva_shape& s, int max_seq_len, bool keys_separate);
+DecodePlan plan_mfma_decode_lens_bound(const gva_shape& s);
+bool plan_mfma_decode_lens(const gva_shape& s, const int32_t* lens, int max_seq_len,
+                           DecodePlan* plan, PlanTable* table);
 hipError_t launch_decode_mfma(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,
                               hipStream_t stream);
 bool prefill_supported(const gva_shape& s, int q_len, bool keys_separate);
@@ -194,16 +197,52 @@ gva_status workspace_size(const gva_shape* shape, int32_t max_seq_len, bool keys
   return GVA_OK;
 }
 
+// The host-planned split (gva_*_lens): single query token, GVA keys, the
+// matrix-core decode with four heads per value group, B <= kPlanMaxItems.
+gva_status check_lens_shape(const gva_shape* shape) {
+  if (!shape) return GVA_ERR_NULL;
+  gva_status st = check_cache_shape(*shape);
+  if (st != GVA_OK) return st;
+  st = check_rope_width(shape->d_r);
+  if (st != GVA_OK) return st;
+  if (shape->B > gva::kPlanMaxItems || shape->H != 4 * shape->G ||
+      !gva::mfma_decode_supported(*shape, false, 1))
+    return GVA_ERR_UNSUPPORTED;
+  return GVA_OK;
+}
+
+// The plan for a decode call: from max_seq_len, or (lens_host) from the
+// host copy of the lengths into `table`.
+gva_status plan_decode(const gva_shape& s, int32_t max_seq_len, bool keys_separate,
+                       int32_t q_len, const int32_t* lens_host, gva::DecodePlan* plan,
+                       gva::PlanTable* table) {
+  if (!lens_host) return make_plan(s, max_seq_len, keys_separate, q_len, plan);
+  if (s.B == 0) {
+    *plan = gva::plan_mfma_decode_lens_bound(s);
+    return GVA_OK;
+  }
+  if (!gva::plan_mfma_decode_lens(s, lens_host, max_seq_len, plan, table)) return GVA_ERR_SHAPE;
+  return GVA_OK;
+}
+
 gva_status decode(const gva_shape* shape, int32_t q_len, const float* q, float q_scale,
                   const void* k_pool, const void* v_pool, const int32_t* block_table,
                   const int32_t* seq_lens, int32_t max_seq_len, void* workspace,
                   size_t workspace_bytes, float* out, float* lse, void* stream,
-                  bool keys_separate) {
+                  bool keys_separate, const int32_t* lens_host = nullptr,
+                  bool lens_call = false) {
+  if (lens_call) {
+    gva_status sl = check_lens_shape(shape);
+    if (sl != GVA_OK) return sl;
+    if (shape->B > 0 && !lens_host) return GVA_ERR_NULL;
+  }
   gva_status st = check_decode_args(shape, max_seq_len, keys_separate, q_len);
   if (st != GVA_OK) return st;
   const gva_shape s = columns(*shape, q_len);
   gva::DecodePlan plan;
-  st = make_plan(s, max_seq_len, keys_separate, q_len, &plan);
+  gva::PlanTable table;
+  st = plan_decode(s, max_seq_len, keys_separate, q_len, lens_call ? lens_host : nullptr, &plan,
+                   &table);
   if (st != GVA_OK) return st;
   if (s.B == 0) return GVA_OK;
   // without a positional slice the GVA path reads no key cache
@@ -229,6 +268,7 @@ gva_status decode(const gva_shape* shape, int32_t q_len, const float* q, float q
   a.q_scale = q_scale;
   a.q_len = q_len;
   a.keys_separate = keys_separate;
+  a.plan_table = lens_call ? &table : nullptr;
   hipStream_t strm = static_cast<hipStream_t>(stream);
   if (plan.kernel == gva::kKernelPrefill)
     return to_status(gva::launch_prefill(*shape, q_len, q, v_pool, k_pool, block_table,
@@ -246,16 +286,24 @@ gva_status step_impl(const gva_shape* shape, int32_t q_len, const float* q_nope,
                      const float* v_new, const float* k_new, void* v_pool, void* k_pool,
                      const int32_t* block_table, const int32_t* seq_lens, int32_t max_seq_len,
                      void* workspace, size_t workspace_bytes, float* out, float* lse,
-                     void* stream, bool noalloc) {
+                     void* stream, bool noalloc, const int32_t* lens_host = nullptr,
+                     bool lens_call = false) {
   if (!shape) return GVA_ERR_NULL;
   const gva_shape& s = *shape;
   gva_status st = check_absorb_shape(s, softmax_scale, rope_base);
   if (st != GVA_OK) return st;
+  if (lens_call) {
+    st = check_lens_shape(shape);
+    if (st != GVA_OK) return st;
+    if (s.B > 0 && !lens_host) return GVA_ERR_NULL;
+  }
   st = check_decode_args(shape, max_seq_len, false, q_len);
   if (st != GVA_OK) return st;
   gva::DecodePlan plan;
+  gva::PlanTable table;
   const gva_shape sc = columns(s, q_len);
-  st = make_plan(sc, max_seq_len, false, q_len, &plan);
+  st = plan_decode(sc, max_seq_len, false, q_len, lens_call ? lens_host : nullptr, &plan,
+                   &table);
   if (st != GVA_OK) return st;
   if (s.B == 0) return GVA_OK;
   if (!q_nope || (s.d_r > 0 && (!q_rope || !k_pool)) || !M || !v_pool || !block_table ||
@@ -301,6 +349,7 @@ gva_status step_impl(const gva_shape* shape, int32_t q_len, const float* q_nope,
   a.q_scale = 1.0f;
   a.q_len = q_len;
   a.keys_separate = false;
+  a.plan_table = lens_call ? &table : nullptr;
   if (plan.kernel == gva::kKernelPrefill)
     return to_status(gva::launch_prefill(s, q_len, qa, v_pool, k_pool, block_table, seq_lens,
                                          max_seq_len, false, 1.0f, out, lse, strm));
@@ -432,6 +481,45 @@ gva_status gva_decode_attention_multi(const gva_shape* shape, int32_t q_len, con
                                       void* stream) {
   return decode(shape, q_len, qa, 1.0f, k_pool, v_pool, block_table, seq_lens, max_seq_len,
                 workspace, workspace_bytes, out, lse, stream, false);
+}
+
+gva_status gva_decode_workspace_size_lens(const gva_shape* shape, size_t* bytes) {
+  if (!bytes) return GVA_ERR_NULL;
+  gva_status st = check_lens_shape(shape);
+  if (st != GVA_OK) return st;
+  *bytes = gva::plan_mfma_decode_lens_bound(*shape).workspace_bytes;
+  return GVA_OK;
+}
+
+gva_status gva_decode_attention_lens(const gva_shape* shape, const float* qa, const void* v_pool,
+                                     const void* k_pool, const int32_t* block_table,
+                                     const int32_t* seq_lens, const int32_t* seq_lens_host,
+                                     int32_t max_seq_len, void* workspace,
+                                     size_t workspace_bytes, float* out, float* lse,
+                                     void* stream) {
+  return decode(shape, 1, qa, 1.0f, k_pool, v_pool, block_table, seq_lens, max_seq_len,
+                workspace, workspace_bytes, out, lse, stream, false, seq_lens_host, true);
+}
+
+gva_status gva_decode_step_workspace_size_lens(const gva_shape* shape, size_t* bytes) {
+  if (!bytes) return GVA_ERR_NULL;
+  gva_status st = check_lens_shape(shape);
+  if (st != GVA_OK) return st;
+  *bytes = step_qa_offset(gva::plan_mfma_decode_lens_bound(*shape).workspace_bytes) +
+           step_qa_bytes(*shape, 1);
+  return GVA_OK;
+}
+
+gva_status gva_decode_step_lens(const gva_shape* shape, const float* q_nope,
+                                const float* q_rope, const float* M, float softmax_scale,
+                                float rope_base, const float* v_new, const float* k_new,
+                                void* v_pool, void* k_pool, const int32_t* block_table,
+                                const int32_t* seq_lens, const int32_t* seq_lens_host,
+                                int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                                float* out, float* lse, void* stream) {
+  return step_impl(shape, 1, q_nope, q_rope, M, softmax_scale, rope_base, v_new, k_new, v_pool,
+                   k_pool, block_table, seq_lens, max_seq_len, workspace, workspace_bytes, out,
+                   lse, stream, false, seq_lens_host, true);
 }
 
 gva_status gva_decode_attention(const gva_shape* shape, const float* qa, const void* v_pool,

@@ -536,7 +536,14 @@ __device__ __forceinline__ void last_step(const WaveCtx& w, const QOps<GT, DH, D
 // NW: waves per block.  WPE: waves per SIMD the register budget is sized
 // for (2 where the tiles fit in 256 registers without spilling, else 1).
 // NSET: register tile sets in rotation (3, or 2 where three would spill).
-template <int GT, int DH, int DR, bool GQA, int NW, int WPE, int NSET, bool VALU = false>
+// VALU: scores on the vector units (the matrix-core ablation).  PLAN: the
+// split comes from a host plan (PlanTable) instead of the grid's (chunk,
+// sequence) coordinates.
+template <bool P> struct PlanSel { typedef NoPlan type; };
+template <> struct PlanSel<true> { typedef PlanTable type; };
+
+template <int GT, int DH, int DR, bool GQA, int NW, int WPE, int NSET, bool VALU = false,
+          bool PLAN = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void decode_mfma_kernel(
     const float* __restrict__ q, const bf16_t* __restrict__ v_pool,
@@ -544,7 +551,9 @@ void decode_mfma_kernel(
     const int32_t* __restrict__ seq_lens, int max_seq_len, int H, int G, int max_blocks,
     int num_blocks, int chunk_tokens, int num_chunks, int max_groups, int q_len, float q_scale,
     float* __restrict__ part,
-    unsigned* __restrict__ tickets, float* __restrict__ out, float* __restrict__ lse) {
+    unsigned* __restrict__ tickets, float* __restrict__ out, float* __restrict__ lse,
+    typename PlanSel<PLAN>::type plan) {
+  static_assert(!PLAN || (!GQA && GT == 4), "host-planned split: single-token GVA");
   using C = Cfg<GT, DH, DR, GQA>;
   using BC = BlockCfg<C, NW>;
   constexpr int kThreads = BC::THREADS;
@@ -557,7 +566,19 @@ void decode_mfma_kernel(
   // result does not depend on the mapping (the merge uses device-scope
   // accesses); it only changes where the work runs.
   int c = blockIdx.x, b = blockIdx.y;
-  if ((num_chunks * gridDim.y) % 8 == 0) {
+  int item = 0, plan_nc = 0;  // PLAN: this block's plan item and its sequence's chunk count
+  if constexpr (PLAN) {
+    // items of one sequence are consecutive; the same renumbering puts
+    // consecutive items on one XCD
+    const int n = gridDim.x;
+    item = blockIdx.x;
+    if (n % 8 == 0) item = (item % 8) * (n / 8) + item / 8;
+    const unsigned it = plan.item[item];
+    if (it == kPlanNoItem) return;  // padding (uniform; before any barrier)
+    b = static_cast<int>(it & 0xffu);
+    c = static_cast<int>((it >> 8) & 0xffu);
+    plan_nc = static_cast<int>(it >> 16);
+  } else if ((num_chunks * gridDim.y) % 8 == 0) {
     const int n8 = num_chunks * gridDim.y / 8;
     const int lin = blockIdx.x + blockIdx.y * num_chunks;
     const int p = (lin % 8) * n8 + lin / 8;  // a permutation of 0 .. grid - 1
@@ -603,6 +624,9 @@ void decode_mfma_kernel(
   int len = seq_lens[b];
   int bad = (len < 0 || len > max_seq_len || len > max_blocks * kBlock ||
              (len > 0 && len < q_len)) ? 1 : 0;
+  // PLAN: the device length must give the plan's chunk count (else the
+  // sequence is reported NaN, and no block of it takes a ticket)
+  if (PLAN && !bad && (len + chunk_tokens - 1) / chunk_tokens != plan_nc) bad = 1;
   if (bad) len = 0;
   // A block past its sequence's end runs no step (no tiles) and leaves
   // after the loop; there is no branch before it, so nothing above can be
@@ -747,7 +771,8 @@ void decode_mfma_kernel(
         float4{st.acc[dt][0], st.acc[dt][1], st.acc[dt][2], st.acc[dt][3]};
   __syncthreads();
   const float* all = reinterpret_cast<const float*>(lds_raw);
-  float* pb = part + (static_cast<size_t>(b) * num_chunks + c) * H * C::REC;
+  float* pb = part + (PLAN ? static_cast<size_t>(item)
+                           : static_cast<size_t>(b) * num_chunks + c) * H * C::REC;
   const float nan = __builtin_nanf("");
   // VW output dims per thread: 2 where that gives every thread of the block
   // one item (d_h = 64 with 8 waves), else 4 (d_h = 64 with 4 waves: again
@@ -812,8 +837,15 @@ void decode_mfma_kernel(
   const int nc = (len + chunk_tokens - 1) / chunk_tokens;
   const int ng = (max_groups > 0 && nc > 2 * kGroupChunks) ? (nc + kGroupChunks - 1) / kGroupChunks : 1;
   const size_t rset = static_cast<size_t>(H) * C::REC;  // floats of one record set
-  unsigned* seq_ticket = tickets + static_cast<size_t>(b) * (1 + max_groups) * kTicketStride;
+  // PLAN: records, group records and counters are indexed by plan item (the
+  // sequence's items are p0 .. p0 + nc - 1): chunk records at p0 + c, group
+  // records after all items at p0 + group, the sequence's counter at p0 and
+  // its group counters at p0 + 1 + group (ng < nc)
+  const size_t p0 = PLAN ? static_cast<size_t>(item - c) : 0;
+  unsigned* seq_ticket =
+      tickets + (PLAN ? p0 : static_cast<size_t>(b) * (1 + max_groups)) * kTicketStride;
   float* groups = part + static_cast<size_t>(gridDim.y) * num_chunks * rset;
+  if constexpr (PLAN) groups = part + (static_cast<size_t>(plan.n_items) + p0) * rset;
   // whether this block drew the last of n tickets (every thread sees it)
   auto last_of = [&](unsigned* t, int n) -> bool {
     if (threadIdx.x == 0)
@@ -883,20 +915,22 @@ void decode_mfma_kernel(
   };
   wait_stores();
   __syncthreads();
-  const float* seq_records = part + static_cast<size_t>(b) * num_chunks * rset;
+  const float* seq_records =
+      part + (PLAN ? p0 : static_cast<size_t>(b) * num_chunks) * rset;
   if (ng > 1) {
     const int gi = c / kGroupChunks;
     const int ncg = min(kGroupChunks, nc - gi * kGroupChunks);
     unsigned* gt = seq_ticket + (1 + gi) * kTicketStride;
     if (!last_of(gt, ncg)) return;
-    float* grec = groups + (static_cast<size_t>(b) * max_groups + gi) * rset;
+    float* grec = groups + (PLAN ? static_cast<size_t>(gi)
+                                 : static_cast<size_t>(b) * max_groups + gi) * rset;
     merge(seq_records + static_cast<size_t>(gi) * kGroupChunks * rset, ncg, grec);
     if (threadIdx.x == 0)  // ready for the next call
       __hip_atomic_store(gt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     wait_stores();
     __syncthreads();
     if (!last_of(seq_ticket, ng)) return;
-    merge(groups + static_cast<size_t>(b) * max_groups * rset, ng, nullptr);
+    merge(groups + (PLAN ? 0 : static_cast<size_t>(b) * max_groups * rset), ng, nullptr);
   } else {
     if (!last_of(seq_ticket, nc)) return;
     merge(seq_records, nc, nullptr);
@@ -917,6 +951,22 @@ hipError_t launch_shape(const gva_shape& s, const DecodePlan& plan, const Decode
                         hipStream_t stream) {
   dim3 grid(plan.num_chunks, s.B);
   if ((s.H / 16) > NW || NW % (s.H / 16) != 0) return hipErrorInvalidValue;
+  if (a.plan_table) {  // the host-planned split: one block per plan item
+    if constexpr (!GQA && GT == 4) {
+      const int n = a.plan_table->n_items;
+      const int padded = (n + 7) / 8 * 8;
+      if (n < 1 || padded > kPlanMaxItems) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((decode_mfma_kernel<GT, DH, DR, GQA, NW, WPE, NSET, false, true>),
+                         dim3(padded), dim3(64 * NW), 0, stream,
+                         a.q, static_cast<const bf16_t*>(a.v_pool),
+                         static_cast<const bf16_t*>(a.k_pool), a.block_table, a.seq_lens,
+                         a.max_seq_len, s.H, s.G, s.max_blocks, s.num_blocks,
+                         plan.chunk_tokens, plan.num_chunks, plan.max_groups, a.q_len,
+                         a.q_scale, a.partials, a.tickets, a.out, a.lse, *a.plan_table);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   auto kernel = decode_mfma_kernel<GT, DH, DR, GQA, NW, WPE, NSET, false>;
   if constexpr (!GQA && GT == 4 && NSET == 2) {
     if (valu_scores_requested()) kernel = decode_mfma_kernel<GT, DH, DR, GQA, NW, WPE, NSET, true>;
@@ -926,7 +976,7 @@ hipError_t launch_shape(const gva_shape& s, const DecodePlan& plan, const Decode
                      static_cast<const bf16_t*>(a.k_pool), a.block_table, a.seq_lens,
                      a.max_seq_len, s.H, s.G, s.max_blocks, s.num_blocks, plan.chunk_tokens,
                      plan.num_chunks, plan.max_groups, a.q_len, a.q_scale, a.partials, a.tickets,
-                     a.out, a.lse);
+                     a.out, a.lse, NoPlan{});
   return hipGetLastError();
 }
 
@@ -1029,6 +1079,56 @@ DecodePlan plan_mfma_decode(const gva_shape& s, int max_seq_len, bool keys_separ
   p.ticket_bytes = ticket_bytes(s.B, p.max_groups);
   p.workspace_bytes = p.ticket_bytes + p.partial_floats * sizeof(float);
   return p;
+}
+
+// The split planned from the host copy of the lengths (ragged batches):
+// the smallest chunk (a multiple of the cache block) for which the batch's
+// (sequence, chunk) items, at least one per sequence, number at most
+// kPlanMaxItems, so that every item holds about the same number of tokens
+// and the grid is one block per compute unit.  Workspace: a bound that does
+// not depend on the lengths (counters and records for kPlanMaxItems items,
+// and as many group records).  Returns false where it does not apply
+// (B > kPlanMaxItems, or a length outside [0, max_seq_len]).
+DecodePlan plan_mfma_decode_lens_bound(const gva_shape& s) {
+  DecodePlan p{};
+  p.kernel = kKernelMfma;
+  p.max_groups = 1;  // two-level merge wherever a sequence has more than 2 groups' chunks
+  p.num_chunks = 1;
+  p.partial_floats = static_cast<size_t>(2) * kPlanMaxItems * s.H * (s.d_h + 4);
+  p.ticket_bytes = static_cast<size_t>(kPlanMaxItems) * kTicketStride * 4;
+  p.workspace_bytes = p.ticket_bytes + p.partial_floats * sizeof(float);
+  return p;
+}
+
+bool plan_mfma_decode_lens(const gva_shape& s, const int32_t* lens, int max_seq_len,
+                           DecodePlan* plan, PlanTable* table) {
+  if (s.B < 1 || s.B > kPlanMaxItems) return false;
+  long long total = 0;
+  for (int b = 0; b < s.B; ++b) {
+    if (lens[b] < 0 || lens[b] > max_seq_len) return false;
+    total += lens[b];
+  }
+  long long chunk = (total + kPlanMaxItems - 1) / kPlanMaxItems;
+  chunk = ((chunk + kBlock - 1) / kBlock) * kBlock;
+  if (chunk < kBlock) chunk = kBlock;
+  auto items = [&](long long ch) {
+    long long n = 0;
+    for (int b = 0; b < s.B; ++b) n += lens[b] > 0 ? (lens[b] + ch - 1) / ch : 1;
+    return n;
+  };
+  while (items(chunk) > kPlanMaxItems) chunk += kBlock;  // ends by chunk >= max length
+  *plan = plan_mfma_decode_lens_bound(s);
+  plan->chunk_tokens = static_cast<int>(chunk);
+  int n = 0;
+  for (int b = 0; b < s.B; ++b) {
+    const int nc = lens[b] > 0 ? static_cast<int>((lens[b] + chunk - 1) / chunk) : 0;
+    for (int c = 0; c < (nc > 0 ? nc : 1); ++c)
+      table->item[n++] = static_cast<unsigned>(b) | (static_cast<unsigned>(c) << 8) |
+                         (static_cast<unsigned>(nc) << 16);
+  }
+  table->n_items = n;
+  for (int i = n; i < kPlanMaxItems; ++i) table->item[i] = kPlanNoItem;
+  return true;
 }
 
 hipError_t launch_decode_mfma(const gva_shape& s, const DecodePlan& plan, const DecodeArgs& a,

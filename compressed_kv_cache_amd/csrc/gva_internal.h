@@ -21,6 +21,19 @@ struct DecodePlan {
   int max_groups;         // chunk groups per sequence of a two-level merge (0: one level)
 };
 
+// A split planned on the host from the sequence lengths (ragged batches):
+// item i of the launch is chunk c of sequence b, whose chunk count is nc;
+// a sequence's items are consecutive.  Records, group records and counters
+// are indexed by item (see the decode kernel).  Padding items (to a
+// multiple of 8 blocks) are kPlanNoItem.
+constexpr int kPlanMaxItems = 256;
+constexpr unsigned kPlanNoItem = 0xffffffffu;
+struct PlanTable {
+  unsigned item[kPlanMaxItems];  // b | c << 8 | nc << 16
+  int n_items;                   // items before the padding
+};
+struct NoPlan {};
+
 // Workspace = [B x (1 + max_groups) counters, one per 256 B][partial
 // records][group records].  A counter per 256 B keeps the blocks of
 // different sequences from contending for one memory channel.  The
@@ -82,6 +95,7 @@ struct DecodeArgs {
   float q_scale;          // multiplies q inside the kernel
   int q_len;              // query tokens per sequence (causal, the last q_len positions)
   bool keys_separate;
+  const PlanTable* plan_table;  // split planned on the host (nullptr: from max_seq_len)
 };
 
 // Log-sum-exp merge of the per-chunk partial records

@@ -160,10 +160,16 @@ def _workspace(nbytes, dev, workspace):
     return workspace
 
 
-def decode_attention(qa, v_pool, k_pool, block_table, seq_lens, max_seq_len,
-                     workspace=None, out=None, lse=None, want_lse=True):
-    """out[B,H,d_h] (and lse[B,H]) of the absorbed query over the paged
-    value cache and shared positional-key cache (gva_decode_attention)."""
+def _host_lens(seq_lens_host, B):
+    """The host copy of the lengths as a contiguous CPU int32 tensor."""
+    t = torch.as_tensor(seq_lens_host, dtype=torch.int32).cpu().contiguous()
+    if t.dim() != 1 or t.shape[0] != B:
+        raise ValueError("seq_lens_host must hold one length per sequence")
+    return t
+
+
+def _decode(qa, v_pool, k_pool, block_table, seq_lens, max_seq_len, workspace, out, lse,
+            want_lse, seq_lens_host):
     dev = qa.device
     _need(qa, "qa", torch.float32, dev, 3)
     _need(v_pool, "v_pool", v_pool.dtype, dev, 4)
@@ -178,20 +184,60 @@ def decode_attention(qa, v_pool, k_pool, block_table, seq_lens, max_seq_len,
     s = _decode_shape(B, H, v_pool, d_r, block_table)
     lib = _lib.load()
     n = ctypes.c_size_t(0)
-    check("gva_decode_workspace_size",
-          lib.gva_decode_workspace_size(ctypes.byref(s), int(max_seq_len), ctypes.byref(n)))
+    if seq_lens_host is None:
+        check("gva_decode_workspace_size",
+              lib.gva_decode_workspace_size(ctypes.byref(s), int(max_seq_len), ctypes.byref(n)))
+    else:
+        hl = _host_lens(seq_lens_host, B)
+        check("gva_decode_workspace_size_lens",
+              lib.gva_decode_workspace_size_lens(ctypes.byref(s), ctypes.byref(n)))
     workspace = _workspace(n.value, dev, workspace)
     if out is None:
         out = torch.empty((B, H, d_h), dtype=torch.float32, device=dev)
     if lse is None and want_lse:
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    st = lib.gva_decode_attention(
-        ctypes.byref(s), _ptr(qa), _ptr(v_pool), _ptr(k_pool), _ptr(block_table),
-        _ptr(seq_lens), int(max_seq_len), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
-        _stream(dev))
-    check("gva_decode_attention", st)
+    if seq_lens_host is None:
+        st = lib.gva_decode_attention(
+            ctypes.byref(s), _ptr(qa), _ptr(v_pool), _ptr(k_pool), _ptr(block_table),
+            _ptr(seq_lens), int(max_seq_len), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+            _stream(dev))
+        check("gva_decode_attention", st)
+    else:
+        st = lib.gva_decode_attention_lens(
+            ctypes.byref(s), _ptr(qa), _ptr(v_pool), _ptr(k_pool), _ptr(block_table),
+            _ptr(seq_lens), hl.data_ptr(), int(max_seq_len), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+            _stream(dev))
+        check("gva_decode_attention_lens", st)
     return out, lse
+
+
+def decode_attention(qa, v_pool, k_pool, block_table, seq_lens, max_seq_len,
+                     workspace=None, out=None, lse=None, want_lse=True):
+    """out[B,H,d_h] (and lse[B,H]) of the absorbed query over the paged
+    value cache and shared positional-key cache (gva_decode_attention)."""
+    return _decode(qa, v_pool, k_pool, block_table, seq_lens, max_seq_len, workspace, out,
+                   lse, want_lse, None)
+
+
+def decode_attention_lens(qa, v_pool, k_pool, block_table, seq_lens, seq_lens_host,
+                          max_seq_len, workspace=None, out=None, lse=None, want_lse=True):
+    """decode_attention with the context split planned from the host copy of
+    the lengths (gva_decode_attention_lens; ragged batches).  seq_lens_host:
+    the same lengths in host memory (a CPU tensor or a sequence)."""
+    return _decode(qa, v_pool, k_pool, block_table, seq_lens, max_seq_len, workspace, out,
+                   lse, want_lse, seq_lens_host)
+
+
+def decode_workspace_bytes_lens(B, H, v_pool, k_pool, block_table):
+    """Workspace size gva_decode_attention_lens needs for these caches (any
+    lengths; zero-fill once when allocated)."""
+    s = _decode_shape(B, H, v_pool, k_pool.shape[2], block_table)
+    n = ctypes.c_size_t(0)
+    check("gva_decode_workspace_size_lens", _lib.load().gva_decode_workspace_size_lens(
+        ctypes.byref(s), ctypes.byref(n)))
+    return n.value
 
 
 def gqa_decode_attention(q, k_pool, v_pool, block_table, seq_lens, max_seq_len,
@@ -238,11 +284,8 @@ def decode_step_workspace_bytes(q_nope, q_rope, v_pool, k_pool, block_table, max
     return n.value
 
 
-def decode_step(q_nope, q_rope, M, v_pool, k_pool, block_table, seq_lens, max_seq_len,
-                v_new=None, k_new=None, softmax_scale=None, rope_base=10000.0,
-                workspace=None, out=None, lse=None, want_lse=True):
-    """Append (if v_new/k_new are given) + absorb + decode in two launches
-    (gva_decode_step).  The new token and the query sit at seq_lens - 1."""
+def _step(q_nope, q_rope, M, v_pool, k_pool, block_table, seq_lens, max_seq_len, v_new,
+          k_new, softmax_scale, rope_base, workspace, out, lse, want_lse, seq_lens_host):
     dev = v_pool.device
     _need(q_nope, "q_nope", torch.float32, dev, 3)
     _need(q_rope, "q_rope", torch.float32, dev, 3)
@@ -269,20 +312,64 @@ def decode_step(q_nope, q_rope, M, v_pool, k_pool, block_table, seq_lens, max_se
                  _cache_dtype(v_pool, "v_pool"))
     lib = _lib.load()
     n = ctypes.c_size_t(0)
-    check("gva_decode_step_workspace_size", lib.gva_decode_step_workspace_size(
-        ctypes.byref(s), int(max_seq_len), ctypes.byref(n)))
+    if seq_lens_host is None:
+        check("gva_decode_step_workspace_size", lib.gva_decode_step_workspace_size(
+            ctypes.byref(s), int(max_seq_len), ctypes.byref(n)))
+    else:
+        hl = _host_lens(seq_lens_host, B)
+        check("gva_decode_step_workspace_size_lens", lib.gva_decode_step_workspace_size_lens(
+            ctypes.byref(s), ctypes.byref(n)))
     workspace = _workspace(n.value, dev, workspace)
     if out is None:
         out = torch.empty((B, H, d_h), dtype=torch.float32, device=dev)
     if lse is None and want_lse:
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    st = lib.gva_decode_step(
-        ctypes.byref(s), _ptr(q_nope), _ptr(q_rope), _ptr(M), float(softmax_scale or 0.0),
-        float(rope_base), _ptr(v_new), _ptr(k_new), _ptr(v_pool), _ptr(k_pool),
-        _ptr(block_table), _ptr(seq_lens), int(max_seq_len), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(dev))
-    check("gva_decode_step", st)
+    if seq_lens_host is None:
+        st = lib.gva_decode_step(
+            ctypes.byref(s), _ptr(q_nope), _ptr(q_rope), _ptr(M), float(softmax_scale or 0.0),
+            float(rope_base), _ptr(v_new), _ptr(k_new), _ptr(v_pool), _ptr(k_pool),
+            _ptr(block_table), _ptr(seq_lens), int(max_seq_len), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(dev))
+        check("gva_decode_step", st)
+    else:
+        st = lib.gva_decode_step_lens(
+            ctypes.byref(s), _ptr(q_nope), _ptr(q_rope), _ptr(M), float(softmax_scale or 0.0),
+            float(rope_base), _ptr(v_new), _ptr(k_new), _ptr(v_pool), _ptr(k_pool),
+            _ptr(block_table), _ptr(seq_lens), hl.data_ptr(), int(max_seq_len),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+            _stream(dev))
+        check("gva_decode_step_lens", st)
     return out, lse
+
+
+def decode_step(q_nope, q_rope, M, v_pool, k_pool, block_table, seq_lens, max_seq_len,
+                v_new=None, k_new=None, softmax_scale=None, rope_base=10000.0,
+                workspace=None, out=None, lse=None, want_lse=True):
+    """Append (if v_new/k_new are given) + absorb + decode in two launches
+    (gva_decode_step).  The new token and the query sit at seq_lens - 1."""
+    return _step(q_nope, q_rope, M, v_pool, k_pool, block_table, seq_lens, max_seq_len, v_new,
+                 k_new, softmax_scale, rope_base, workspace, out, lse, want_lse, None)
+
+
+def decode_step_lens(q_nope, q_rope, M, v_pool, k_pool, block_table, seq_lens, seq_lens_host,
+                     max_seq_len, v_new=None, k_new=None, softmax_scale=None,
+                     rope_base=10000.0, workspace=None, out=None, lse=None, want_lse=True):
+    """decode_step with the context split planned from the host copy of the
+    lengths (gva_decode_step_lens; ragged batches)."""
+    return _step(q_nope, q_rope, M, v_pool, k_pool, block_table, seq_lens, max_seq_len, v_new,
+                 k_new, softmax_scale, rope_base, workspace, out, lse, want_lse, seq_lens_host)
+
+
+def decode_step_workspace_bytes_lens(q_nope, q_rope, v_pool, k_pool, block_table):
+    """Workspace size gva_decode_step_lens needs (any lengths; zero-fill once)."""
+    B, H, d_n = q_nope.shape
+    NB, bs, G, d_h = v_pool.shape
+    s = GvaShape(B, H, G, d_h, d_n, q_rope.shape[2], bs, block_table.shape[1], NB,
+                 _cache_dtype(v_pool, "v_pool"))
+    n = ctypes.c_size_t(0)
+    check("gva_decode_step_workspace_size_lens", _lib.load().gva_decode_step_workspace_size_lens(
+        ctypes.byref(s), ctypes.byref(n)))
+    return n.value
 
 
 def decode_step_noalloc(q_nope, q_rope, M, v_pool, k_pool, block_table, seq_lens,

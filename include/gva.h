@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define GVA_ABI_VERSION 3
+#define GVA_ABI_VERSION 4
 
 typedef enum gva_status {
   GVA_OK = 0,
@@ -224,6 +224,54 @@ gva_status gva_decode_step(const gva_shape* shape, const float* q_nope,
                            int32_t max_seq_len, void* workspace,
                            size_t workspace_bytes, float* out, float* lse,
                            void* stream);
+
+/* The decode and the step with the context split planned from the host copy
+ * of the sequence lengths, for ragged batches.  The decode reads the whole
+ * cache every step and is bound by that read (onedev.kr review, "Premises
+ * and limits"); the pages leave longer and uneven contexts unmeasured
+ * (agihunt.info summary, the "three gaps" paragraph).  gva_decode_attention
+ * sizes its chunks from max_seq_len alone, so on a ragged batch the blocks
+ * of the longest sequences hold most of the work while others sit idle.
+ * Here the chunk is the smallest multiple of block_size for which the
+ * batch's (sequence, chunk) items, at least one per sequence, number at most
+ * 256 (one block per compute unit); every item then holds about the same
+ * number of tokens.  The results equal gva_decode_attention's up to the
+ * fp32 summation order (a different split), and are bitwise reproducible
+ * for the same lengths.
+ *   seq_lens_host [B] i32 in host memory, read during the call only: each
+ *   in [0, max_seq_len] (else GVA_ERR_SHAPE, before any HIP call), and
+ *   equal to seq_lens on the device.  A sequence whose device length gives
+ *   another chunk count than its host length gets NaN outputs, like any
+ *   other invalid length.
+ *   workspace: at least gva_decode_workspace_size_lens (decode) or
+ *   gva_decode_step_workspace_size_lens (step) bytes, zero-filled at
+ *   allocation; these sizes depend on the shape only (not on the lengths).
+ * Supported: one query token, bf16 cache, H = 4 G, the shapes the
+ * matrix-core decode covers, B <= 256; other shapes give
+ * GVA_ERR_UNSUPPORTED.  Other arguments, layouts and errors as
+ * gva_decode_attention and gva_decode_step. */
+gva_status gva_decode_workspace_size_lens(const gva_shape* shape, size_t* bytes);
+gva_status gva_decode_attention_lens(const gva_shape* shape, const float* qa,
+                                     const void* v_pool, const void* k_pool,
+                                     const int32_t* block_table,
+                                     const int32_t* seq_lens,
+                                     const int32_t* seq_lens_host,
+                                     int32_t max_seq_len, void* workspace,
+                                     size_t workspace_bytes, float* out,
+                                     float* lse, void* stream);
+gva_status gva_decode_step_workspace_size_lens(const gva_shape* shape,
+                                               size_t* bytes);
+gva_status gva_decode_step_lens(const gva_shape* shape, const float* q_nope,
+                                const float* q_rope, const float* M,
+                                float softmax_scale, float rope_base,
+                                const float* v_new, const float* k_new,
+                                void* v_pool, void* k_pool,
+                                const int32_t* block_table,
+                                const int32_t* seq_lens,
+                                const int32_t* seq_lens_host,
+                                int32_t max_seq_len, void* workspace,
+                                size_t workspace_bytes, float* out, float* lse,
+                                void* stream);
 
 /* For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  The same

@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(g):
 
 
 def test_version_and_status_strings(g):
-    assert g.lib.gva_abi_version() == 3
+    assert g.lib.gva_abi_version() == 4
     for code in range(8):
         assert g.lib.gva_status_string(code)
     assert g.lib.gva_status_string(99) == b"unknown status"
@@ -369,3 +369,50 @@ def test_noalloc_step_validates_like_the_step(g):
     assert _step_noalloc(g, _shape(g), ptrs) == 4
     assert _step_noalloc(g, _shape(g, H=15), NOALLOC_GOOD) == 2
     assert _step_noalloc(g, _shape(g), NOALLOC_GOOD, max_seq_len=257) == 2
+
+
+# ---- the host-planned split (gva_*_lens): argument checks, no GPU ----
+
+def _ws_lens(g, s):
+    n = ctypes.c_size_t(0)
+    st = g.lib.gva_decode_workspace_size_lens(ctypes.byref(s), ctypes.byref(n))
+    return st, n.value
+
+
+def test_lens_workspace_depends_on_the_shape_only(g):
+    st, n = _ws_lens(g, _shape(g, B=8))
+    assert st == 0 and n > 0
+    # records and counters for 256 items, and as many group records
+    assert n >= 256 * 256 + 2 * 256 * 16 * (64 + 4) * 4
+    assert _ws_lens(g, _shape(g, B=1)) == (0, n)
+    m = ctypes.c_size_t(0)
+    assert g.lib.gva_decode_step_workspace_size_lens(ctypes.byref(_shape(g, B=8)),
+                                                     ctypes.byref(m)) == 0
+    assert m.value >= n + 8 * 16 * (64 + 16) * 4
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=257),                                   # more sequences than plan items
+    dict(G=2),                                     # H = 8 G: not the single-token instances
+    dict(cache_dtype=__import__("torch").float32),  # no matrix-core decode
+    dict(d_h=32, d_n=24, d_r=8),                   # no matrix-core instance
+])
+def test_lens_unsupported_shapes(g, kw):
+    assert _ws_lens(g, _shape(g, **kw))[0] == 3
+
+
+def _call_lens(g, s, lens, max_seq_len=256):
+    P = ctypes.c_void_p
+    host = (ctypes.c_int32 * len(lens))(*lens) if lens is not None else None
+    return g.lib.gva_decode_attention_lens(
+        ctypes.byref(s), P(0x10000), P(0x10000), P(0x10000), P(0x10000), P(0x10000),
+        host, max_seq_len, P(0x10000), 1 << 30, P(0x10000), None, None)
+
+
+def test_lens_host_lengths_are_checked_before_any_launch(g):
+    s = _shape(g, B=3)
+    assert _call_lens(g, s, [10, 300, 5]) == 2       # a length past max_seq_len
+    assert _call_lens(g, s, [10, -1, 5]) == 2        # a negative length
+    assert _call_lens(g, s, None) == 1               # no host lengths
+    assert _call_lens(g, _shape(g, B=0), None) == 0  # nothing to do
+    assert _call_lens(g, _shape(g, B=257), [1] * 257) == 3

@@ -1025,3 +1025,142 @@ def test_vector_unit_scores(g, gpu, monkeypatch, name, kw):
     if cfg.T is None and cfg.len_range is None:
         extra = {"seq_lens": torch.tensor(EDGE_LENS, dtype=torch.int32), "shuffled": True}
     _check_all(g, gpu, cfg, **extra)
+
+
+# ------------------------------------------ split planned from host lengths ----
+# gva_decode_attention_lens / gva_decode_step_lens: the chunk is sized from
+# the host copy of the lengths so that every (sequence, chunk) item holds
+# about the same tokens (ragged batches).  Same bars against the oracle; the
+# results differ from the max_seq_len split only by summation order.
+
+def _lens_case(gpu, name, kw, lens=None):
+    cfg = syn.with_overrides(syn.get_config(name), **kw)
+    extra = {}
+    if lens is not None:
+        extra = {"seq_lens": torch.tensor(lens, dtype=torch.int32), "shuffled": True}
+    x, h = gen(cfg, gpu, **extra)
+    return cfg, x, h
+
+
+@pytest.mark.parametrize("name,kw,lens,heads", [
+    ("long_ragged", {}, None, [0, 7, 15]),
+    ("decode_350m", {"B": len(EDGE_LENS), "T": None, "len_range": None}, EDGE_LENS, None),
+    ("decode_350m", {"B": 4, "T": None, "len_range": None}, [0, 5, 0, 1000], None),
+    ("decode_350m", {"B": 5, "T": None, "len_range": None}, [70000, 100, 5, 0, 3000], [0, 9]),
+    ("decode_350m", {"B": 32, "T": 2048}, None, None),
+    ("wide_rope_append", {"B": 12, "T": None, "len_range": (1, 6000), "append": False}, None,
+     None),
+])
+def test_decode_with_host_planned_split(g, gpu, name, kw, lens, heads):
+    cfg, x, h = _lens_case(gpu, name, kw, lens)
+    announce("host-planned split", name, kw, lens)
+    qa = g.absorb_query(x["q_nope"], x["q_rope"], x["M"], x["pos"], rope_base=cfg.rope_base)
+    host = x["seq_lens_host"]
+    ws = torch.zeros(g.decode_workspace_bytes_lens(cfg.B, cfg.H, x["v_pool"], x["k_pool"],
+                                                   x["block_table"]),
+                     dtype=torch.uint8, device=gpu)
+    out, lse = g.decode_attention_lens(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                       x["seq_lens"], host, x["max_seq_len"], workspace=ws)
+    torch.cuda.synchronize()
+    vp, kp = oracle_pools(h, cfg)
+    ref, ref_lse = o.gva_decode_materialized(
+        h["q_nope"], h["q_rope"], h["M"], vp, kp, h["block_table"], h["seq_lens"],
+        base=cfg.rope_base, heads=heads)
+    got, got_lse = cpu(out).double().numpy(), cpu(lse).double().numpy()
+    sel = np.isfinite(ref_lse)
+    assert_bf16_parity(got[sel], ref[sel])
+    assert_bf16_split_precision(got[sel], ref[sel])
+    np.testing.assert_allclose(got_lse[sel], ref_lse[sel], rtol=0, atol=1e-3)
+    for b in range(cfg.B):  # empty sequences: zeros and -inf
+        if int(host[b]) == 0:
+            assert torch.all(out[b] == 0) and torch.all(lse[b] == -float("inf"))
+    # the max_seq_len split: the same up to summation order
+    out2, _ = g.decode_attention(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                 x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    live = torch.tensor([int(v) > 0 for v in host], device=gpu)
+    d = (out - out2)[live].abs().max().item()
+    assert d <= 1e-5 * max(1.0, out2[live].abs().max().item())
+    # the workspace is reused as is (every counter left zero): same bits
+    out3, lse3 = g.decode_attention_lens(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                         x["seq_lens"], host, x["max_seq_len"], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out3) and torch.equal(lse.nan_to_num(7), lse3.nan_to_num(7))
+
+
+def test_host_planned_split_flags_a_length_mismatch(g, gpu):
+    """A sequence whose device length gives another chunk count than its
+    host length gets NaN; the others are unaffected."""
+    lens = [3000, 2000, 500, 64]
+    cfg, x, h = _lens_case(gpu, "decode_350m", {"B": 4, "T": None, "len_range": None}, lens)
+    qa = g.absorb_query(x["q_nope"], x["q_rope"], x["M"], x["pos"], rope_base=cfg.rope_base)
+    good, _ = g.decode_attention_lens(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                      x["seq_lens"], lens, x["max_seq_len"])
+    wrong = list(lens)
+    wrong[0] = 40          # far fewer chunks than the device length needs
+    out, lse = g.decode_attention_lens(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                       x["seq_lens"], wrong, x["max_seq_len"])
+    torch.cuda.synchronize()
+    assert torch.isnan(out[0]).all() and torch.isnan(lse[0]).all()
+    # the other sequences see another chunk size, so compare to tolerance
+    assert torch.allclose(out[1:], good[1:], rtol=0, atol=1e-5)
+
+
+def test_step_with_host_planned_split(g, gpu):
+    cfg, x, h = _lens_case(gpu, "wide_rope_append", {"B": 10, "T": None, "len_range": (1, 5000)})
+    vp0, kp0 = x["v_pool"].clone(), x["k_pool"].clone()
+    host = x["seq_lens_host"]
+    out, lse = g.decode_step_lens(x["q_nope"], x["q_rope"], x["M"], x["v_pool"], x["k_pool"],
+                                  x["block_table"], x["seq_lens"], host, x["max_seq_len"],
+                                  v_new=x["v_new"], k_new=x["k_new"], rope_base=cfg.rope_base)
+    torch.cuda.synchronize()
+    x2 = dict(x)
+    x2["v_pool"], x2["k_pool"] = vp0, kp0
+    out2, _ = g.decode_step(x2["q_nope"], x2["q_rope"], x2["M"], x2["v_pool"], x2["k_pool"],
+                            x2["block_table"], x2["seq_lens"], x2["max_seq_len"],
+                            v_new=x2["v_new"], k_new=x2["k_new"], rope_base=cfg.rope_base)
+    torch.cuda.synchronize()
+    assert torch.equal(x["v_pool"].nan_to_num(7), x2["v_pool"].nan_to_num(7))
+    assert torch.allclose(out, out2, rtol=0, atol=1e-5)
+    vp, kp = oracle_pools(h, cfg)
+    ref, ref_lse = o.gva_decode_materialized(
+        h["q_nope"], h["q_rope"], h["M"], vp, kp, h["block_table"], h["seq_lens"],
+        base=cfg.rope_base)
+    got = cpu(out).double().numpy()
+    assert_bf16_parity(got, ref)
+    assert_bf16_split_precision(got, ref)
+
+
+def test_host_planned_split_in_a_graph(g, gpu):
+    """The plan travels in the kernel arguments: replays of a captured call
+    equal the eager call."""
+    cfg, x, h = _lens_case(gpu, "long_ragged", {"len_range": (100, 20000)})
+    qa = g.absorb_query(x["q_nope"], x["q_rope"], x["M"], x["pos"], rope_base=cfg.rope_base)
+    host = x["seq_lens_host"]
+    ws = torch.zeros(g.decode_workspace_bytes_lens(cfg.B, cfg.H, x["v_pool"], x["k_pool"],
+                                                   x["block_table"]),
+                     dtype=torch.uint8, device=gpu)
+    out = torch.empty((cfg.B, cfg.H, cfg.d_h), device=gpu)
+    lse = torch.empty((cfg.B, cfg.H), device=gpu)
+
+    def call():
+        g.decode_attention_lens(qa, x["v_pool"], x["k_pool"], x["block_table"], x["seq_lens"],
+                                host, x["max_seq_len"], workspace=ws, out=out, lse=lse)
+
+    call()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for i in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i}"
