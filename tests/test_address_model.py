@@ -136,11 +136,32 @@ def piece_geometry(GT, DH):
     return max(rows), min(lo), max(hi), ROWB
 
 
+def plan_lens(lens_host, max_items=256):
+    """The split planned from host lengths (gva_decode_attention_lens): the
+    smallest chunk, a multiple of the cache block, for which the items (at
+    least one per sequence) number at most max_items; items (b, c, nc) in
+    sequence order."""
+    total = int(sum(int(n) for n in lens_host))
+    chunk = max(KB, -(-(-(-total // max_items)) // KB) * KB)
+
+    def count(ch):
+        return sum(-(-int(n) // ch) if n > 0 else 1 for n in lens_host)
+    while count(chunk) > max_items:
+        chunk += KB
+    items = []
+    for b, n in enumerate(lens_host):
+        nc = -(-int(n) // chunk) if n > 0 else 0
+        items += [(b, c, nc) for c in range(max(nc, 1))]
+    return chunk, items
+
+
 def decode_reads(lens, bt, nb, G, DH, DR, cols, gqa=False, q_len=1, max_seq_len=None,
-                 redirect=True):
+                 redirect=True, lens_host=None):
     """Checks every load of one split-decode launch; returns the number of
     tile loads checked.  redirect=False models a kernel without the row-0
-    redirect of tiles past the range (the planted mistake of a test below)."""
+    redirect of tiles past the range (the planted mistake of a test below).
+    lens_host: the split planned from these host lengths instead (device
+    lengths `lens` whose chunk count differs are invalid)."""
     inst = mfma_instance(cols, G, DH, DR, gqa, q_len)
     assert inst is not None, "no split matrix-core instance for this shape"
     GT, NW, NSET = inst
@@ -151,8 +172,22 @@ def decode_reads(lens, bt, nb, G, DH, DR, cols, gqa=False, q_len=1, max_seq_len=
         n = int(n)
         bad = n < 0 or n > max_seq_len or n > max_blocks * KB or (0 < n < q_len)
         return 0 if bad else n
-    chunk, num_chunks = plan_mfma(B, max_seq_len)
-    blocks = [(b, c) for b in range(B) for c in range(num_chunks)]
+    plan_nc = {}
+    if lens_host is None:
+        chunk, num_chunks = plan_mfma(B, max_seq_len)
+        blocks = [(b, c) for b in range(B) for c in range(num_chunks)]
+    else:
+        chunk, items = plan_lens(lens_host)
+        assert len(items) <= 256
+        blocks = [(b, c) for b, c, _ in items]
+        for p, (b, c, nc) in enumerate(items):
+            plan_nc[b] = nc
+            # records at p0 + c and p0 + group (after all items), counters at
+            # p0 and p0 + 1 + group: inside the shape-only workspace bound
+            p0 = p - c
+            assert p0 + c < 256 and len(items) + p0 + max(0, -(-nc // 16) - 1) < 2 * 256
+            if nc > 32:
+                assert -(-nc // 16) < nc and p0 + -(-nc // 16) < 256
     assert chunk % TILE == 0
     nht = cols // 16
     nsub = NW // nht
@@ -169,6 +204,8 @@ def decode_reads(lens, bt, nb, G, DH, DR, cols, gqa=False, q_len=1, max_seq_len=
     checked = 0
     for b, c in blocks:
         length = valid(lens[b])
+        if lens_host is not None and length and -(-length // chunk) != plan_nc[b]:
+            length = 0  # the kernel reports the sequence NaN and loads nothing for it
         j_begin = c * chunk
         active = j_begin < length
         j_end = min(length, j_begin + chunk)
@@ -340,6 +377,39 @@ def test_decode_reads_with_two_level_merges(B, T):
     chunk, num_chunks = plan_mfma(B, T)
     decode_reads(lens, bt, nb, 4, 64, 16, 16)
     assert num_chunks > 32 or B * T < 256 * 64 * 40
+
+
+@pytest.mark.parametrize("lens", [
+    "long_ragged", EDGE_LENS, [70000, 100, 5, 0, 3000], [0, 0, 1], [131072] * 2,
+    list(range(1, 257)),
+])
+@pytest.mark.parametrize("H,G,d_h,d_r", [(16, 4, 64, 16), (16, 4, 64, 24), (32, 8, 128, 32)])
+def test_decode_reads_with_host_planned_split(lens, H, G, d_h, d_r):
+    if isinstance(lens, str):
+        lens = np.random.default_rng(1).integers(1024, 131072, endpoint=True, size=8)
+    lens = np.array(lens)
+    bt, nb = make_table(lens)
+    ms = int(max(lens.max(), 1))
+    assert decode_reads(lens, bt, nb, G, d_h, d_r, H, max_seq_len=ms, lens_host=lens) >= 0
+    # device lengths that disagree with the plan (longer and shorter)
+    dev = lens.copy()
+    dev[0] = min(ms, int(dev[0]) + 5000)
+    dev[-1] = max(0, int(dev[-1]) - 3000)
+    decode_reads(dev, bt, nb, G, d_h, d_r, H, max_seq_len=ms, lens_host=lens)
+
+
+def test_host_plan_balances_the_items():
+    """Every item holds at most one chunk of tokens, the chunk is the
+    smallest multiple of the block with at most 256 items, and a uniform
+    batch gets the max_seq_len split."""
+    lens = np.random.default_rng(1).integers(1024, 131072, endpoint=True, size=8)
+    chunk, items = plan_lens(lens)
+    assert len(items) <= 256 and chunk % KB == 0
+    assert plan_lens(lens, 256)[0] == chunk
+    smaller = chunk - KB
+    if smaller >= KB:
+        assert sum(-(-int(n) // smaller) for n in lens) > 256
+    assert plan_lens(np.full(32, 4096))[0] == plan_mfma(32, 4096)[0]
 
 
 def test_every_instance_has_in_row_pieces():
