@@ -1116,7 +1116,21 @@ bool plan_mfma_decode_lens(const gva_shape& s, const int32_t* lens, int max_seq_
     for (int b = 0; b < s.B; ++b) n += lens[b] > 0 ? (lens[b] + ch - 1) / ch : 1;
     return n;
   };
-  while (items(chunk) > kPlanMaxItems) chunk += kBlock;  // ends by chunk >= max length
+  if (items(chunk) > kPlanMaxItems) {
+    // the item count does not grow with the chunk, and a chunk of the
+    // longest length gives one item per sequence (<= kPlanMaxItems): binary
+    // search, in blocks, for the smallest chunk that fits
+    long long lo = chunk / kBlock, hi = (max_seq_len + kBlock - 1) / kBlock;
+    if (hi < lo) hi = lo;
+    while (lo < hi) {
+      const long long mid = (lo + hi) / 2;
+      if (items(mid * kBlock) > kPlanMaxItems)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    chunk = lo * kBlock;
+  }
   *plan = plan_mfma_decode_lens_bound(s);
   plan->chunk_tokens = static_cast<int>(chunk);
   int n = 0;

@@ -1048,6 +1048,8 @@ def _lens_case(gpu, name, kw, lens=None):
     ("decode_350m", {"B": 4, "T": None, "len_range": None}, [0, 5, 0, 1000], None),
     ("decode_350m", {"B": 5, "T": None, "len_range": None}, [70000, 100, 5, 0, 3000], [0, 9]),
     ("decode_350m", {"B": 32, "T": 2048}, None, None),
+    # 255 one-token sequences and a long one: the chunk search ends at the long length
+    ("decode_350m", {"B": 256, "T": None, "len_range": None}, [1] * 255 + [20000], [0, 5]),
     ("wide_rope_append", {"B": 12, "T": None, "len_range": (1, 6000), "append": False}, None,
      None),
 ])
