@@ -80,6 +80,9 @@ def parse():
                     help="skip the decode timed with its scores on the vector units")
     ap.add_argument("--no-host-planned", action="store_true",
                     help="skip the decode timed with its split planned from host lengths")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the long ragged workload's decode (both splits) beside "
+                         "the 350M-shaped one")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--ingest-counters", nargs=4, metavar="DIR")
@@ -377,6 +380,17 @@ def main():
     if (not args.no_host_planned and cfg.cache_dtype == "bfloat16" and cfg.H == 4 * cfg.G
             and cfg.B <= 256):
         extra["host_planned_split"] = bench_host_planned(torch, gva, syn, cfg0, dev, args.steps)
+    if not args.no_long_context and cfg.name == "decode_350m":
+        # the long-context workload (8 sequences of 1024 .. 131072 tokens,
+        # shuffled blocks) at the 350M head shape: the split sized from
+        # max_seq_len and the one planned from the host lengths
+        if pools is not None:
+            del pools
+            torch.cuda.empty_cache()
+            pools = None
+        lc = syn.get_config("long_ragged")
+        extra["long_context"] = {"workload": lc.name,
+                                 **bench_host_planned(torch, gva, syn, lc, dev, args.steps)}
     if not args.no_multi:
         del pools
         torch.cuda.empty_cache()
