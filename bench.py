@@ -39,6 +39,36 @@ METRIC = ("decode-attn cache GB/s (% of HBM peak) and queries*ctx/s, "
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 ROTATE_BYTES = 1 << 30
+
+# Every timed leg times at least this many launches, whatever --steps is: a
+# few graph replays alone read high (measured: 58.8 against 50.8 us per
+# decode at the wide-rope shape with 3 replays against 25).
+MIN_TIMED_LAUNCHES = 128
+
+
+# Untimed replays before each timed region, for about this long: the GPU's
+# clocks settle only after a spell of load (a decode timed right after a
+# 20-step run read 54.7-58.8 us against 50.8 us after a 200-step run, at the
+# wide-rope shape).
+WARM_SECONDS = 0.1
+
+
+def warm(torch, replay, seconds=WARM_SECONDS):
+    """Replays `replay` (untimed) until `seconds` of wall time have passed."""
+    t = time.perf_counter()
+    while True:
+        for _ in range(4):
+            replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t >= seconds:
+            return
+
+
+def replays(steps, per_replay, at_least=1):
+    """Graph replays to time: enough for `steps` launches and for
+    MIN_TIMED_LAUNCHES, and at least `at_least`."""
+    return max(at_least, -(-steps // per_replay), -(-MIN_TIMED_LAUNCHES // per_replay))
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["compressed_kv_cache_amd/csrc/gva_decode_mfma.hip",
                   "compressed_kv_cache_amd/csrc/gva_decode_ref.hip",
@@ -286,9 +316,8 @@ def main():
     g_step.replay()
     torch.cuda.synchronize()
     graph_matches_eager = bool(torch.equal(out, eager_out))
-    reps = max(1, -(-args.steps // S))
-    for _ in range(2):
-        g_step.replay()
+    reps = replays(args.steps, S)
+    warm(torch, g_step.replay)
     if g_rem is not None:
         g_rem.replay()
     torch.cuda.synchronize()
@@ -302,11 +331,10 @@ def main():
     steps_timed = full * S + rem
     ms_per_step = t0.elapsed_time(t1) / steps_timed
 
-    # decode launches alone: one event pair per graph of R launches
+    # decode launches alone: one event pair per graph of S launches
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
-    g_dec.replay()
-    torch.cuda.synchronize()
+    warm(torch, g_dec.replay)
     for i in range(reps):
         evs[i][0].record()
         g_dec.replay()
@@ -472,9 +500,8 @@ def bench_read_probe(torch, gva, v_pools, dev, steps):
         with torch.cuda.graph(g):
             for i in range(launches):
                 gva.stream_read_probe(bufs[i % len(bufs)], out=out)
-        g.replay()
-        torch.cuda.synchronize()
-        reps = max(1, -(-steps // launches))
+        warm(torch, g.replay)
+        reps = replays(steps, launches)
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record()
@@ -511,9 +538,8 @@ def time_calls(torch, call, steps, S=16):
     with torch.cuda.graph(g):
         for i in range(S):
             call(i)
-    g.replay()
-    torch.cuda.synchronize()
-    reps = max(2, -(-steps // S))
+    warm(torch, g.replay)
+    reps = replays(steps, S, 2)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -562,9 +588,8 @@ def time_decode(torch, gva, c, y, dev, steps, lens_host=None):
     with torch.cuda.graph(g):
         for i in range(S):
             launch(i)
-    g.replay()
-    torch.cuda.synchronize()
-    reps = max(2, -(-steps // S))
+    warm(torch, g.replay)
+    reps = replays(steps, S, 2)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -684,9 +709,8 @@ def bench_multi(torch, gva, syn, cfg, dev, steps, warmup, L):
     with torch.cuda.graph(g):
         for i in range(S):
             launch(i)
-    g.replay()
-    torch.cuda.synchronize()
-    reps = max(1, -(-steps // S))
+    warm(torch, g.replay)
+    reps = replays(steps, S)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -718,9 +742,7 @@ def bench_prefill(torch, gva, syn, cfg, dev, calls=10):
         gva.decode_attention_multi(qa, y["v_pool"], y["k_pool"], y["block_table"],
                                    y["seq_lens"], y["max_seq_len"], out=out, lse=lse)
 
-    for _ in range(2):
-        launch()
-    torch.cuda.synchronize()
+    warm(torch, launch)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -743,9 +765,7 @@ def bench_prefill(torch, gva, syn, cfg, dev, calls=10):
         gva.gqa_decode_attention_multi(z["q"], z["k_pool"], z["v_pool"], z["block_table"],
                                        z["seq_lens"], z["max_seq_len"], out=out, lse=lse)
 
-    for _ in range(2):
-        launch_gqa()
-    torch.cuda.synchronize()
+    warm(torch, launch_gqa)
     t0.record()
     for _ in range(calls):
         launch_gqa()
@@ -793,7 +813,7 @@ def bench_rope_keys(torch, gva, syn, cfg, dev, steps):
 
     res = {}
     S = max(R, 8)
-    reps = max(1, -(-steps // S) // 4)
+    reps = max(1, replays(steps, S) // 4)
     for name, fn in (("rope_on_keys", rope), ("absorbed", absorbed)):
         for i in range(S):
             fn(i)
@@ -802,8 +822,7 @@ def bench_rope_keys(torch, gva, syn, cfg, dev, steps):
         with torch.cuda.graph(gr):
             for i in range(S):
                 fn(i)
-        gr.replay()
-        torch.cuda.synchronize()
+        warm(torch, gr.replay)
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record()
@@ -851,9 +870,8 @@ def bench_gqa(torch, gva, syn, cfg, dev, steps, warmup):
     with torch.cuda.graph(g):
         for i in range(S):
             launch(i)
-    g.replay()
-    torch.cuda.synchronize()
-    reps = max(1, -(-steps // S))
+    warm(torch, g.replay)
+    reps = replays(steps, S)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
