@@ -405,20 +405,25 @@ def main():
                                            extra.get("gqa", {}).get("us_avg"))
     if not args.no_vector_scores and cfg.cache_dtype == "bfloat16" and cfg.H == 4 * cfg.G:
         extra["vector_scores"] = bench_vector_scores(torch, gva, syn, cfg0, dev, args.steps)
+    # the split planned from host lengths: on ragged workloads only (on equal
+    # lengths the plan is the max_seq_len split)
     if (not args.no_host_planned and cfg.cache_dtype == "bfloat16" and cfg.H == 4 * cfg.G
-            and cfg.B <= 256):
+            and cfg.B <= 256 and cfg.T is None):
         extra["host_planned_split"] = bench_host_planned(torch, gva, syn, cfg0, dev, args.steps)
     if not args.no_long_context and cfg.name == "decode_350m":
         # the long-context workload (8 sequences of 1024 .. 131072 tokens,
-        # shuffled blocks) at the 350M head shape: the split sized from
-        # max_seq_len and the one planned from the host lengths
+        # shuffled blocks) at the 350M head shape, with its split planned
+        # from the host lengths (its own kernel instance, so every launch of
+        # the headline instance in this run is at the headline shape; the
+        # max_seq_len split of this workload: --workload long_ragged)
         if pools is not None:
             del pools
             torch.cuda.empty_cache()
             pools = None
         lc = syn.get_config("long_ragged")
         extra["long_context"] = {"workload": lc.name,
-                                 **bench_host_planned(torch, gva, syn, lc, dev, args.steps)}
+                                 **bench_host_planned(torch, gva, syn, lc, dev, args.steps,
+                                                      with_max_len=False)}
     if not args.no_multi:
         del pools
         torch.cuda.empty_cache()
@@ -630,21 +635,24 @@ def bench_dr_sweep(torch, gva, syn, cfg, dev, steps, gqa_us):
             "gqa_us_avg_same_shape": gqa_us, "rows": rows}
 
 
-def bench_host_planned(torch, gva, syn, cfg, dev, steps):
+def bench_host_planned(torch, gva, syn, cfg, dev, steps, with_max_len=True):
     """The decode with its split planned from the host copy of the lengths
-    (gva_decode_attention_lens) beside the split sized from max_seq_len, on
-    the workload's own lengths, same protocol as the headline decode."""
+    (gva_decode_attention_lens), beside the split sized from max_seq_len
+    unless with_max_len is false, on the workload's own lengths, same
+    protocol as the headline decode."""
     y = syn.make_gva_inputs(cfg, device=dev)
     host = y["seq_lens_host"]
     tokens = int(host.sum())
     byts = tokens * (cfg.G * cfg.d_h + cfg.d_r) * 2
     res = {"tokens": tokens, "max_len": int(host.max()), "cache_bytes": byts}
-    for name, lens in (("split_by_max_seq_len", None), ("host_planned", host)):
+    splits = (("split_by_max_seq_len", None),) if with_max_len else ()
+    for name, lens in splits + (("host_planned", host),):
         us = time_decode(torch, gva, cfg, y, dev, steps, lens)
         res[name] = {"us_avg": us, "GBps": byts / (us * 1e-6) / 1e9,
                      "frac_of_peak": byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
-    res["time_ratio_planned_over_max_len"] = (res["host_planned"]["us_avg"] /
-                                              res["split_by_max_seq_len"]["us_avg"])
+    if with_max_len:
+        res["time_ratio_planned_over_max_len"] = (res["host_planned"]["us_avg"] /
+                                                  res["split_by_max_seq_len"]["us_avg"])
     del y
     torch.cuda.empty_cache()
     return res
