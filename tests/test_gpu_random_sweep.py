@@ -1,0 +1,147 @@
+"""Seeded random sweep of the single-query decode against the float64 oracle.
+
+Each case draws, from its own seed: a head shape (every width the kernels
+serve), the cache dtype, the batch size, a length recipe (uniform with empty
+sequences, tile and block edges, or one long sequence among short ones),
+shuffled or contiguous block tables, slack in max_seq_len, whether the step
+appends a token, and the call path -- the three separate calls, the
+two-launch step, or their forms with the split planned from host lengths.
+The result is compared element by element with the oracle that
+materialises K_h = V_g(h) M_h, at the same bars as the fixed cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as o
+import synthetic as syn
+from parity_util import (announce, assert_bf16_parity, assert_bf16_split_precision,
+                         assert_fp32_parity, cpu)
+
+pytestmark = pytest.mark.gpu
+
+# (H, G, d_h, d_n, d_r)
+SHAPES = [
+    (16, 4, 64, 48, 16),
+    (16, 4, 64, 40, 24),
+    (16, 4, 64, 32, 32),
+    (16, 4, 64, 64, 0),
+    (16, 4, 64, 64, 16),     # content and position slices wider than d_h
+    (32, 8, 128, 96, 32),
+    (16, 4, 128, 112, 16),
+    (64, 16, 64, 48, 16),
+    (8, 8, 32, 24, 8),       # one head per group: the vector-unit kernel
+    (16, 2, 64, 62, 2),
+]
+EDGES = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 511, 512, 513]
+N_CASES = 32
+
+
+def draw_case(i):
+    rng = np.random.default_rng(9100 + i)
+    H, G, d_h, d_n, d_r = SHAPES[int(rng.integers(len(SHAPES)))]
+    dtype = "float32" if rng.random() < 0.2 else "bfloat16"
+    B = int(rng.integers(1, 13))
+    recipe = int(rng.integers(3))
+    if recipe == 0:
+        lens = rng.integers(1, 2049, size=B)
+        lens[rng.random(B) < 0.2] = 0  # empty sequences
+    elif recipe == 1:
+        lens = rng.choice(EDGES, size=B)
+    else:
+        lens = np.concatenate([rng.integers(4000, 9001, size=1),
+                               rng.integers(1, 200, size=B - 1)])
+        rng.shuffle(lens)
+    append = bool(rng.random() < 0.5)
+    if append:
+        lens = np.maximum(lens, 1)
+    shuffled = bool(rng.random() < 0.5)
+    slack = int(rng.integers(1, 300)) if rng.random() < 0.3 else 0
+    planned_ok = dtype == "bfloat16" and H == 4 * G and d_h in (64, 128)
+    path = ["calls", "step", "calls_lens", "step_lens"][int(rng.integers(4 if planned_ok else 2))]
+    return dict(H=H, G=G, d_h=d_h, d_n=d_n, d_r=d_r, dtype=dtype, B=B,
+                lens=[int(v) for v in lens], append=append, shuffled=shuffled,
+                slack=slack, path=path)
+
+
+@pytest.fixture(scope="module")
+def g(gpu):
+    import compressed_kv_cache_amd as pkg
+    return pkg
+
+
+def test_sweep_covers_every_path_and_dtype():
+    """The drawn cases reach every call path, both dtypes, appends, slack
+    and each length recipe's extremes (so the sweep is not silently narrow)."""
+    cases = [draw_case(i) for i in range(N_CASES)]
+    assert {c["path"] for c in cases} == {"calls", "step", "calls_lens", "step_lens"}
+    assert {c["dtype"] for c in cases} == {"float32", "bfloat16"}
+    assert any(c["append"] for c in cases) and not all(c["append"] for c in cases)
+    assert any(c["slack"] for c in cases)
+    assert any(0 in c["lens"] for c in cases)
+    assert any(max(c["lens"]) >= 4000 for c in cases)
+    drawn = {(c["H"], c["G"], c["d_h"], c["d_n"], c["d_r"]) for c in cases}
+    assert drawn == set(SHAPES)
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_case(g, gpu, i):
+    c = draw_case(i)
+    announce("random sweep", i, c)
+    cfg = syn.with_overrides(syn.get_config("decode_350m"), B=c["B"], H=c["H"], G=c["G"],
+                             d_h=c["d_h"], d_n=c["d_n"], d_r=c["d_r"], T=None,
+                             len_range=None, cache_dtype=c["dtype"], append=c["append"],
+                             seed=9100 + i)
+    lens = torch.tensor(c["lens"], dtype=torch.int32)
+    x = syn.make_gva_inputs(cfg, device=gpu, seq_lens=lens, shuffled=c["shuffled"])
+    h = {k: cpu(v) for k, v in x.items() if isinstance(v, torch.Tensor)}
+    max_seq_len = x["max_seq_len"] + c["slack"]
+    bt = x["block_table"]
+    if c["slack"]:
+        # room for max_seq_len: unused columns holding a valid block id
+        extra = torch.zeros((c["B"], -(-c["slack"] // 64)), dtype=bt.dtype, device=bt.device)
+        bt = torch.cat([bt, extra], dim=1).contiguous()
+    assert max_seq_len <= bt.shape[1] * 64
+    host = x["seq_lens_host"]
+    new = dict(v_new=x["v_new"], k_new=x["k_new"]) if c["append"] else {}
+    if c["path"].startswith("step"):
+        if c["path"] == "step":
+            out, lse = g.decode_step(x["q_nope"], x["q_rope"], x["M"], x["v_pool"], x["k_pool"],
+                                     bt, x["seq_lens"], max_seq_len,
+                                     rope_base=cfg.rope_base, **new)
+        else:
+            out, lse = g.decode_step_lens(x["q_nope"], x["q_rope"], x["M"], x["v_pool"],
+                                          x["k_pool"], bt, x["seq_lens"], host,
+                                          max_seq_len, rope_base=cfg.rope_base, **new)
+    else:
+        if c["append"]:
+            g.append_cache(x["v_new"], x["k_new"], x["pos"], bt, x["v_pool"],
+                           x["k_pool"], rope_base=cfg.rope_base)
+        qa = g.absorb_query(x["q_nope"], x["q_rope"], x["M"], x["pos"], rope_base=cfg.rope_base)
+        if c["path"] == "calls":
+            out, lse = g.decode_attention(qa, x["v_pool"], x["k_pool"], bt,
+                                          x["seq_lens"], max_seq_len)
+        else:
+            out, lse = g.decode_attention_lens(qa, x["v_pool"], x["k_pool"], bt,
+                                               x["seq_lens"], host, max_seq_len)
+    torch.cuda.synchronize()
+
+    vp, kp = h["v_pool"], h["k_pool"]
+    if c["append"]:
+        vp, kp = o.append_token(vp, kp, h["v_new"], h["k_new"], h["pos"], h["block_table"],
+                                base=cfg.rope_base, cache_dtype=cfg.cache_dtype)
+    ref, ref_lse = o.gva_decode_materialized(h["q_nope"], h["q_rope"], h["M"], vp, kp,
+                                             h["block_table"], h["seq_lens"],
+                                             base=cfg.rope_base)
+    got, got_lse = cpu(out).double().numpy(), cpu(lse).double().numpy()
+    live = np.asarray(c["lens"]) > 0
+    if c["dtype"] == "float32":
+        assert_fp32_parity(got[live], ref[live])
+        assert_fp32_parity(got_lse[live], ref_lse[live])
+    else:
+        assert_bf16_parity(got[live], ref[live])
+        assert_bf16_split_precision(got[live], ref[live])
+        np.testing.assert_allclose(got_lse[live], ref_lse[live], rtol=0, atol=1e-3)
+    # empty sequences: zeros and -inf
+    for b in np.flatnonzero(~live):
+        assert torch.all(out[b] == 0) and torch.all(lse[b] == -float("inf"))
