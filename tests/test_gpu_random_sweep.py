@@ -18,8 +18,6 @@ import synthetic as syn
 from parity_util import (announce, assert_bf16_parity, assert_bf16_split_precision,
                          assert_fp32_parity, cpu)
 
-pytestmark = pytest.mark.gpu
-
 # (H, G, d_h, d_n, d_r)
 SHAPES = [
     (16, 4, 64, 48, 16),
@@ -84,6 +82,7 @@ def test_sweep_covers_every_path_and_dtype():
     assert drawn == set(SHAPES)
 
 
+@pytest.mark.gpu
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_case(g, gpu, i):
     c = draw_case(i)
