@@ -144,3 +144,89 @@ def test_random_case(g, gpu, i):
     # empty sequences: zeros and -inf
     for b in np.flatnonzero(~live):
         assert torch.all(out[b] == 0) and torch.all(lse[b] == -float("inf"))
+
+
+# ------------------------------------------ several query tokens per step ----
+
+# the single-query widths, and the widths only the blocked kernel serves
+MULTI_SHAPES = SHAPES[:8] + [
+    (8, 4, 64, 48, 16),      # two heads per group
+    (4, 4, 128, 112, 16),    # one head per group
+    (8, 2, 128, 104, 24),    # four heads per group, d_h 128, 24-wide slice
+    (16, 2, 64, 48, 16),     # eight heads per group
+]
+MULTI_L = [2, 3, 4, 5, 8, 16, 17, 33, 64, 65, 100, 200]
+N_MULTI = 24
+
+
+def draw_multi_case(i):
+    rng = np.random.default_rng(9300 + i)
+    H, G, d_h, d_n, d_r = MULTI_SHAPES[int(rng.integers(len(MULTI_SHAPES)))]
+    L = int(rng.choice(MULTI_L))
+    dtype = "float32" if (L <= 4 and rng.random() < 0.3) else "bfloat16"
+    B = int(rng.integers(1, 7))
+    lens = L + rng.integers(0, 1500 if L < 64 else 600, size=B)  # cached prefix
+    lens[rng.random(B) < 0.25] = L           # the prompt alone
+    append = bool(rng.random() < 0.4)
+    if not append:
+        lens[rng.random(B) < 0.15] = 0       # empty sequences
+    return dict(H=H, G=G, d_h=d_h, d_n=d_n, d_r=d_r, L=L, dtype=dtype, B=B,
+                lens=[int(v) for v in lens], append=append,
+                shuffled=bool(rng.random() < 0.5),
+                path="step" if append or rng.random() < 0.3 else "calls")
+
+
+def test_multi_sweep_covers_both_kernels_and_paths():
+    cases = [draw_multi_case(i) for i in range(N_MULTI)]
+    assert {c["path"] for c in cases} == {"calls", "step"}
+    assert {c["dtype"] for c in cases} == {"float32", "bfloat16"}
+    assert any(c["append"] for c in cases)
+    assert any(c["L"] <= 4 for c in cases) and any(c["L"] >= 64 for c in cases)
+    assert any(0 in c["lens"] for c in cases)
+    assert any(c["L"] in c["lens"] for c in cases)
+    assert len({(c["H"], c["G"], c["d_h"], c["d_n"], c["d_r"]) for c in cases}) >= 9
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_MULTI))
+def test_random_multi_case(g, gpu, i):
+    c = draw_multi_case(i)
+    announce("random multi-query sweep", i, c)
+    L = c["L"]
+    cfg = syn.with_overrides(syn.get_config("long_ragged"), B=c["B"], H=c["H"], G=c["G"],
+                             d_h=c["d_h"], d_n=c["d_n"], d_r=c["d_r"], T=None,
+                             len_range=None, cache_dtype=c["dtype"], append=c["append"],
+                             seed=9300 + i)
+    x = syn.make_gva_multi_inputs(cfg, L, device=gpu,
+                                  seq_lens=torch.tensor(c["lens"], dtype=torch.int32),
+                                  shuffled=c["shuffled"])
+    h = {k: cpu(v) for k, v in x.items() if isinstance(v, torch.Tensor)}
+    if c["path"] == "step":
+        new = dict(v_new=x["v_new"], k_new=x["k_new"]) if c["append"] else {}
+        out, lse = g.decode_step_multi(x["q_nope"], x["q_rope"], x["M"], x["v_pool"],
+                                       x["k_pool"], x["block_table"], x["seq_lens"],
+                                       x["max_seq_len"], rope_base=cfg.rope_base, **new)
+    else:
+        qa = g.absorb_query_multi(x["q_nope"], x["q_rope"], x["M"], x["pos"],
+                                  rope_base=cfg.rope_base)
+        out, lse = g.decode_attention_multi(qa, x["v_pool"], x["k_pool"], x["block_table"],
+                                            x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    vp, kp = h["v_pool"], h["k_pool"]
+    if c["append"]:
+        vp, kp = o.append_tokens(vp, kp, h["v_new"], h["k_new"], h["pos"], h["block_table"],
+                                 base=cfg.rope_base, cache_dtype=cfg.cache_dtype)
+    ref, ref_lse = o.gva_decode_materialized_queries(
+        h["q_nope"], h["q_rope"], h["M"], vp, kp, h["block_table"], h["seq_lens"],
+        base=cfg.rope_base)
+    got, got_lse = cpu(out).double().numpy(), cpu(lse).double().numpy()
+    live = np.asarray(c["lens"]) > 0
+    if c["dtype"] == "float32":
+        assert_fp32_parity(got[live], ref[live])
+        assert_fp32_parity(got_lse[live], ref_lse[live])
+    else:
+        assert_bf16_parity(got[live], ref[live])
+        assert_bf16_split_precision(got[live], ref[live])
+        np.testing.assert_allclose(got_lse[live], ref_lse[live], rtol=0, atol=1e-3)
+    for b in np.flatnonzero(~live):
+        assert torch.all(out[b] == 0) and torch.all(lse[b] == -float("inf"))
