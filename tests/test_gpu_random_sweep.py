@@ -230,3 +230,108 @@ def test_random_multi_case(g, gpu, i):
         np.testing.assert_allclose(got_lse[live], ref_lse[live], rtol=0, atol=1e-3)
     for b in np.flatnonzero(~live):
         assert torch.all(out[b] == 0) and torch.all(lse[b] == -float("inf"))
+
+
+# ------------------------------------- the comparison kernels (context) ----
+
+GQA_SHAPES = [(16, 4, 64), (32, 8, 128), (64, 16, 64), (16, 4, 128), (16, 2, 64), (8, 8, 32)]
+ROPE_SHAPES = [(16, 4, 64, 64), (16, 4, 64, 48), (32, 8, 128, 64), (8, 1, 64, 32),
+               (16, 4, 64, 32)]
+N_GQA, N_ROPE = 16, 12
+
+
+def draw_lengths(rng, B, long_max=9000):
+    recipe = int(rng.integers(3))
+    if recipe == 0:
+        lens = rng.integers(1, 2049, size=B)
+        lens[rng.random(B) < 0.2] = 0
+    elif recipe == 1:
+        lens = rng.choice(EDGES, size=B)
+    else:
+        lens = np.concatenate([rng.integers(4000, long_max + 1, size=1),
+                               rng.integers(1, 200, size=B - 1)])
+        rng.shuffle(lens)
+    return [int(v) for v in lens]
+
+
+def draw_gqa_case(i):
+    rng = np.random.default_rng(9504 + i)
+    H, G, d_h = GQA_SHAPES[int(rng.integers(len(GQA_SHAPES)))]
+    B = int(rng.integers(1, 13))
+    return dict(H=H, G=G, d_h=d_h, B=B, lens=draw_lengths(rng, B),
+                dtype="float32" if rng.random() < 0.25 else "bfloat16",
+                shuffled=bool(rng.random() < 0.5))
+
+
+def draw_rope_case(i):
+    rng = np.random.default_rng(9700 + i)
+    H, G, d_h, d_k = ROPE_SHAPES[int(rng.integers(len(ROPE_SHAPES)))]
+    B = int(rng.integers(1, 9))
+    return dict(H=H, G=G, d_h=d_h, d_k=d_k, B=B, lens=draw_lengths(rng, B, 5000),
+                shuffled=bool(rng.random() < 0.5))
+
+
+def test_context_sweeps_cover_their_shapes():
+    gq = [draw_gqa_case(i) for i in range(N_GQA)]
+    assert {(c["H"], c["G"], c["d_h"]) for c in gq} == set(GQA_SHAPES)
+    assert {c["dtype"] for c in gq} == {"float32", "bfloat16"}
+    rp = [draw_rope_case(i) for i in range(N_ROPE)]
+    assert {(c["H"], c["G"], c["d_h"], c["d_k"]) for c in rp} == set(ROPE_SHAPES)
+    for cases in (gq, rp):
+        assert any(0 in c["lens"] for c in cases) and any(max(c["lens"]) >= 4000 for c in cases)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_GQA))
+def test_random_gqa_case(g, gpu, i):
+    """The same-shape GQA decode (keys and values cached) against the
+    oracle's textbook GQA routine."""
+    c = draw_gqa_case(i)
+    announce("random GQA sweep", i, c)
+    cfg = syn.with_overrides(syn.get_config("decode_350m"), B=c["B"], H=c["H"], G=c["G"],
+                             d_h=c["d_h"], d_n=c["d_h"], d_r=0, T=None, len_range=None,
+                             cache_dtype=c["dtype"], shuffled_blocks=c["shuffled"],
+                             seed=9504 + i)
+    x = syn.make_gqa_inputs(cfg, device=gpu, seq_lens=torch.tensor(c["lens"], dtype=torch.int32))
+    out, lse = g.gqa_decode_attention(x["q"], x["k_pool"], x["v_pool"], x["block_table"],
+                                      x["seq_lens"], x["max_seq_len"])
+    torch.cuda.synchronize()
+    h = {k: cpu(v) for k, v in x.items() if isinstance(v, torch.Tensor)}
+    ref, ref_lse = o.gqa_decode(h["q"], h["k_pool"], h["v_pool"], h["block_table"],
+                                h["seq_lens"])
+    got, got_lse = cpu(out).double().numpy(), cpu(lse).double().numpy()
+    live = np.asarray(c["lens"]) > 0
+    if c["dtype"] == "float32":
+        assert_fp32_parity(got[live], ref[live])
+    else:
+        assert_bf16_parity(got[live], ref[live])
+        assert_bf16_split_precision(got[live], ref[live])
+        np.testing.assert_allclose(got_lse[live], ref_lse[live], rtol=0, atol=1e-3)
+    for b in np.flatnonzero(~live):
+        assert torch.all(out[b] == 0) and torch.all(lse[b] == -float("inf"))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_ROPE))
+def test_random_rope_keys_case(g, gpu, i):
+    """The decode with ordinary RoPE on the rebuilt keys against the oracle
+    that forms every rotated key."""
+    c = draw_rope_case(i)
+    announce("random rotated-key sweep", i, c)
+    cfg = syn.with_overrides(syn.get_config("long_ragged"), B=c["B"], H=c["H"], G=c["G"],
+                             d_h=c["d_h"], d_n=c["d_k"], d_r=0, T=None, len_range=None,
+                             seed=9700 + i)
+    x = syn.make_gva_inputs(cfg, device=gpu, seq_lens=torch.tensor(c["lens"], dtype=torch.int32),
+                            shuffled=c["shuffled"])
+    out, lse = g.decode_rope_keys(x["q_nope"], x["M"], x["v_pool"], x["block_table"],
+                                  x["seq_lens"], x["max_seq_len"], rope_base=cfg.rope_base)
+    torch.cuda.synchronize()
+    h = {k: cpu(v) for k, v in x.items() if isinstance(v, torch.Tensor)}
+    ref, ref_lse = o.gva_decode_rope_on_keys(h["q_nope"], h["M"], h["v_pool"], h["block_table"],
+                                             h["seq_lens"], base=cfg.rope_base)
+    got, got_lse = cpu(out).double().numpy(), cpu(lse).double().numpy()
+    live = np.asarray(c["lens"]) > 0
+    assert_bf16_parity(got[live], ref[live])
+    np.testing.assert_allclose(got_lse[live], ref_lse[live], rtol=0, atol=1e-3)
+    for b in np.flatnonzero(~live):
+        assert torch.all(out[b] == 0) and torch.all(lse[b] == -float("inf"))
